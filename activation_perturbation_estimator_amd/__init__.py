@@ -1,0 +1,254 @@
+"""libdust: the Dust virtual-population gradient estimator on MI355X (gfx950).
+
+Thin torch-facing binding of the C ABI in ``include/dust.h``.  Each function
+checks dtypes and shapes, allocates outputs (and the call's workspace) with
+torch on the tensors' device, and calls the library on torch's current stream.
+Every step of the estimator runs in libdust's HIP kernels; there is no CPU
+path, and a missing library raises.
+
+The method ("Dust: Pretraining Transformers Without Backpropagation", Q Labs),
+as the pages about it state it (HN-mirror digest of the paper, section 2.2):
+a linear layer's output y_t is jittered to y_t + sigma a_t for every token and
+draw; token s scores a draw by its centred loss decrease c_s; the reward is
+r_t = sum_{s>=t} gamma^(s-t) c_s inside the sequence; the output-error estimate
+is g_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i); the weight gradient is
+G_W = sum_t g_t x_t^T.  The LM head is perturbed on its cached logits and only
+the cross-entropy is recomputed (laoyaoba analysis, mechanism section).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import (DUST_BF16, DUST_F32, DUST_N_MAX, DUST_SIGMA_MAX, DUST_STAGE_EVENTS,
+                   DustError)
+
+__all__ = [
+    "head_estimate", "linear_estimate", "noise", "philox4x32_10", "head_losses", "centre",
+    "reward_scan", "error_estimate", "outer_sum", "check_targets", "head_workspace_size",
+    "linear_workspace_size", "outer_sum_workspace_size", "version", "DustError",
+    "DUST_SIGMA_MAX", "DUST_N_MAX", "DUST_STAGE_EVENTS",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DUST_F32
+    if t.dtype == torch.bfloat16:
+        return DUST_BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _events(stage_events) -> Optional[object]:
+    if stage_events is None:
+        return None
+    import ctypes
+    if len(stage_events) != DUST_STAGE_EVENTS:
+        raise ValueError(f"stage_events needs {DUST_STAGE_EVENTS} events")
+    arr = (ctypes.c_void_p * DUST_STAGE_EVENTS)()
+    for k, ev in enumerate(stage_events):
+        arr[k] = int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev)
+    return arr
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def version() -> str:
+    return _lib.load().dust_version().decode()
+
+
+def head_workspace_size(T: int, V: int, d: int, K: int, gamma: float = 0.0) -> int:
+    return int(_lib.load().dust_head_workspace_size(T, V, d, K, gamma))
+
+
+def linear_workspace_size(T: int, d_in: int, N: int, K: int, gamma: float = 0.0) -> int:
+    return int(_lib.load().dust_linear_workspace_size(T, d_in, N, K, gamma))
+
+
+def outer_sum_workspace_size(T: int, N: int, d: int) -> int:
+    return int(_lib.load().dust_outer_sum_workspace_size(T, N, d))
+
+
+def head_estimate(logits, targets, X, *, sigma: float, K: int, gamma: float = 0.0,
+                  seed: int = 1, seq_len: Optional[int] = None, stream: int = 0,
+                  return_losses: bool = False, stage_events: Optional[Sequence] = None,
+                  workspace=None, out=None):
+    """LM-head estimator on cached logits.
+
+    logits [T,V] (f32/bf16), targets [T] int32, X [T,d] (f32/bf16), all on one
+    GPU.  Returns (g_hat [T,V] f32, G_W [V,d] f32) and, with return_losses,
+    the per-draw losses [K,T].  ``out`` may pass preallocated (g_hat, G_W)."""
+    torch = _torch()
+    lib = _lib.load()
+    T, V = logits.shape
+    d = X.shape[1]
+    if X.shape[0] != T or targets.shape != (T,) or targets.dtype != torch.int32:
+        raise ValueError("shape/dtype mismatch: logits [T,V], targets [T] int32, X [T,d]")
+    L = T if seq_len is None else int(seq_len)
+    dev = logits.device
+    if out is None:
+        g = torch.empty((T, V), dtype=torch.float32, device=dev)
+        G = torch.empty((V, d), dtype=torch.float32, device=dev)
+    else:
+        g, G = out
+    losses = torch.empty((K, T), dtype=torch.float32, device=dev) if return_losses else None
+    nbytes = lib.dust_head_workspace_size(T, V, d, K, gamma)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.dust_head_estimate(
+        _dev(logits, "logits"), _dtype_code(logits), _dev(targets, "targets"), _dev(X, "X"),
+        _dtype_code(X), T, V, d, L, float(sigma), int(K), float(gamma), int(seed), int(stream),
+        _dev(g, "g_hat"), _dev(G, "G_W"), losses.data_ptr() if losses is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev), _events(stage_events))
+    _lib.check("dust_head_estimate", st)
+    return (g, G, losses) if return_losses else (g, G)
+
+
+def linear_estimate(X, c, *, N: int, sigma: float, gamma: float = 0.0, seed: int = 1,
+                    seq_len: Optional[int] = None, stream: int = 0,
+                    stage_events: Optional[Sequence] = None, workspace=None, out=None):
+    """Hidden linear layer: X [T,d_in] (f32/bf16), caller-centred loss decreases
+    c [K,T] f32 measured with dust noise (seed, stream, draws 0..K-1) of width N.
+    Returns (g_hat [T,N] f32, G_W [N,d_in] f32)."""
+    torch = _torch()
+    lib = _lib.load()
+    T, d_in = X.shape
+    K = c.shape[0]
+    if c.shape != (K, T) or c.dtype != torch.float32:
+        raise ValueError("c must be float32 [K,T]")
+    L = T if seq_len is None else int(seq_len)
+    dev = X.device
+    if out is None:
+        g = torch.empty((T, N), dtype=torch.float32, device=dev)
+        G = torch.empty((N, d_in), dtype=torch.float32, device=dev)
+    else:
+        g, G = out
+    nbytes = lib.dust_linear_workspace_size(T, d_in, N, K, gamma)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.dust_linear_estimate(
+        _dev(X, "X"), _dtype_code(X), _dev(c, "c"), T, d_in, int(N), L, float(sigma), int(K),
+        float(gamma), int(seed), int(stream), _dev(g, "g_hat"), _dev(G, "G_W"), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(dev), _events(stage_events))
+    _lib.check("dust_linear_estimate", st)
+    return g, G
+
+
+def noise(*, seed: int, stream: int = 0, draw0: int = 0, ndraw: int, T: int, N: int,
+          device="cuda"):
+    """a[k,t,n] = a^(draw0+k)_t[n] as float32 [ndraw,T,N] on `device`."""
+    torch = _torch()
+    out = torch.empty((ndraw, T, N), dtype=torch.float32, device=device)
+    st = _lib.load().dust_noise(int(seed), int(stream), int(draw0), int(ndraw), int(T), int(N),
+                                out.data_ptr(), _stream(out.device))
+    _lib.check("dust_noise", st)
+    return out
+
+
+def philox4x32_10(seed: int, ctr):
+    """Raw Philox4x32-10 blocks for counters ctr (int32/uint32 tensor [n,4] on GPU)."""
+    torch = _torch()
+    if ctr.dim() != 2 or ctr.shape[1] != 4 or ctr.element_size() != 4:
+        raise ValueError("ctr must be a 32-bit [n,4] tensor")
+    out = torch.empty_like(ctr)
+    st = _lib.load().dust_philox4x32_10(int(seed), _dev(ctr, "ctr"), out.data_ptr(),
+                                        ctr.shape[0], _stream(ctr.device))
+    _lib.check("dust_philox4x32_10", st)
+    return out
+
+
+def head_losses(logits, targets, *, sigma: float, K: int, seed: int = 1, stream: int = 0):
+    """Per-draw perturbed LM-head losses [K,T] f32."""
+    torch = _torch()
+    T, V = logits.shape
+    out = torch.empty((K, T), dtype=torch.float32, device=logits.device)
+    st = _lib.load().dust_head_losses(_dev(logits, "logits"), _dtype_code(logits),
+                                      _dev(targets, "targets"), T, V, float(sigma), int(K),
+                                      int(seed), int(stream), out.data_ptr(),
+                                      _stream(logits.device))
+    _lib.check("dust_head_losses", st)
+    return out
+
+
+def centre(x, out=None):
+    """c[i,t] = mean_j x[j,t] - x[i,t] for per-draw losses x [K,T] f32."""
+    torch = _torch()
+    K, T = x.shape
+    c = torch.empty_like(x) if out is None else out
+    st = _lib.load().dust_centre(_dev(x, "x"), K, T, _dev(c, "c"), _stream(x.device))
+    _lib.check("dust_centre", st)
+    return c
+
+
+def reward_scan(c, *, seq_len: int, gamma: float, out=None):
+    """r = segmented reverse gamma-scan of c [K,T] f32."""
+    torch = _torch()
+    K, T = c.shape
+    r = torch.empty_like(c) if out is None else out
+    st = _lib.load().dust_reward_scan(_dev(c, "c"), K, T, int(seq_len), float(gamma),
+                                      _dev(r, "r"), _stream(c.device))
+    _lib.check("dust_reward_scan", st)
+    return r
+
+
+def error_estimate(r, *, N: int, sigma: float, seed: int = 1, stream: int = 0, out=None):
+    """g_hat[t,n] = -(1/(K sigma)) sum_i r[i,t] a^(i)_t[n] with regenerated noise."""
+    torch = _torch()
+    K, T = r.shape
+    g = torch.empty((T, N), dtype=torch.float32, device=r.device) if out is None else out
+    st = _lib.load().dust_error_estimate(_dev(r, "r"), K, T, int(N), float(sigma), int(seed),
+                                         int(stream), _dev(g, "g_hat"), _stream(r.device))
+    _lib.check("dust_error_estimate", st)
+    return g
+
+
+def outer_sum(g_hat, X, out=None, workspace=None):
+    """G_W = g_hat^T X (sum over tokens), fp32 [N,d]."""
+    torch = _torch()
+    lib = _lib.load()
+    T, N = g_hat.shape
+    d = X.shape[1]
+    G = torch.empty((N, d), dtype=torch.float32, device=g_hat.device) if out is None else out
+    nbytes = lib.dust_outer_sum_workspace_size(T, N, d)
+    ws = _workspace(nbytes, g_hat.device, workspace)
+    st = lib.dust_outer_sum(_dev(g_hat, "g_hat"), _dev(X, "X"), _dtype_code(X), T, N, d,
+                            _dev(G, "G_W"), ws.data_ptr(), ws.numel() * ws.element_size(),
+                            _stream(g_hat.device))
+    _lib.check("dust_outer_sum", st)
+    return G
+
+
+def check_targets(targets, V: int) -> bool:
+    """True when 0 <= targets < V everywhere (waits for the device)."""
+    torch = _torch()
+    flag = torch.empty(1, dtype=torch.int32, device=targets.device)
+    st = _lib.load().dust_check_targets(_dev(targets, "targets"), targets.numel(), int(V),
+                                        flag.data_ptr(), _stream(targets.device))
+    if st == _lib.DUST_ERR_TARGETS:
+        return False
+    _lib.check("dust_check_targets", st)
+    return True

@@ -1,0 +1,270 @@
+// dust_api.cpp -- the C ABI of libdust: argument validation, workspace layout
+// and the launch sequence of each call.  Every check runs on the host before
+// the first HIP call, so a rejected call touches neither the device nor the
+// stream.  Nothing here allocates memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/dust.h"
+#include "dust_launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool sigma_ok(float sigma) {
+  return std::isfinite(sigma) && sigma > 0.f && sigma <= DUST_SIGMA_MAX;
+}
+bool gamma_ok(float gamma) { return std::isfinite(gamma) && gamma >= 0.f && gamma <= 1.f; }
+bool dtype_ok(dust_dtype dt) { return dt == DUST_F32 || dt == DUST_BF16; }
+
+// Index products stay far below 2^62 and the 32-bit counter words hold t and i.
+constexpr int64_t kMaxT = (int64_t)1 << 31;
+constexpr int64_t kMaxK = ((int64_t)1 << 31) - 64;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool width_ok(int64_t N) { return N > 0 && N % 4 == 0 && N <= DUST_N_MAX; }
+
+dust_status hip_status(hipError_t e) { return e == hipSuccess ? DUST_OK : DUST_ERR_HIP; }
+
+hipStream_t as_stream(dust_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+hipError_t record(const dust_event_t* ev, int k, hipStream_t s) {
+  if (ev == nullptr) return hipSuccess;
+  return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[k]), s);
+}
+
+// Workspace layout of the LM-head call:
+//   [0, a)       per-draw loss changes delta [K,T] (non-fused path only),
+//                later centred in place (c) and scanned in place (r)
+//   [a, a + b)   split-K partials of the outer product
+struct HeadPlan {
+  bool fused;
+  size_t delta_bytes;
+  size_t gemm_bytes;
+  size_t total() const { return align_up(delta_bytes) + align_up(gemm_bytes) + kAlign; }
+};
+
+HeadPlan head_plan(int64_t T, int64_t V, int64_t d, int64_t K, float gamma) {
+  HeadPlan p;
+  p.fused = (gamma == 0.f) && dust::head_fused_supported(V);
+  p.delta_bytes = p.fused ? 0 : (size_t)K * (size_t)T * sizeof(float);
+  p.gemm_bytes = dust::outer_sum_workspace_bytes(T, V, d);
+  return p;
+}
+
+struct LinearPlan {
+  size_t r_bytes;
+  size_t gemm_bytes;
+  size_t total() const { return align_up(r_bytes) + align_up(gemm_bytes) + kAlign; }
+};
+
+LinearPlan linear_plan(int64_t T, int64_t d_in, int64_t N, int64_t K, float gamma) {
+  LinearPlan p;
+  p.r_bytes = (gamma == 0.f) ? 0 : (size_t)K * (size_t)T * sizeof(float);
+  p.gemm_bytes = dust::outer_sum_workspace_bytes(T, N, d_in);
+  return p;
+}
+
+void* aligned_base(void* ws) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(ws);
+  return reinterpret_cast<void*>((p + kAlign - 1) / kAlign * kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dust_status_string(dust_status st) {
+  switch (st) {
+    case DUST_OK: return "DUST_OK";
+    case DUST_ERR_INVALID_ARG: return "DUST_ERR_INVALID_ARG";
+    case DUST_ERR_WORKSPACE: return "DUST_ERR_WORKSPACE";
+    case DUST_ERR_HIP: return "DUST_ERR_HIP";
+    case DUST_ERR_UNSUPPORTED: return "DUST_ERR_UNSUPPORTED";
+    case DUST_ERR_TARGETS: return "DUST_ERR_TARGETS";
+  }
+  return "DUST_ERR_UNKNOWN";
+}
+
+const char* dust_version(void) { return "libdust 1.0 gfx950"; }
+
+size_t dust_head_workspace_size(int64_t T, int64_t V, int64_t d, int64_t K, float gamma) {
+  if (T < 0 || V <= 0 || d <= 0 || K <= 0) return kAlign;
+  return head_plan(T, V, d, K, gamma).total();
+}
+
+size_t dust_linear_workspace_size(int64_t T, int64_t d_in, int64_t N, int64_t K, float gamma) {
+  if (T < 0 || N <= 0 || d_in <= 0 || K <= 0) return kAlign;
+  return linear_plan(T, d_in, N, K, gamma).total();
+}
+
+size_t dust_outer_sum_workspace_size(int64_t T, int64_t N, int64_t d) {
+  if (T < 0 || N <= 0 || d <= 0) return kAlign;
+  return align_up(dust::outer_sum_workspace_bytes(T, N, d)) + kAlign;
+}
+
+dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const int32_t* targets,
+                               const void* X, dust_dtype x_dt, int64_t T, int64_t V, int64_t d,
+                               int64_t seq_len, float sigma, int64_t K, float gamma,
+                               uint64_t seed, uint32_t stream, float* g_hat, float* G_W,
+                               float* losses_opt, void* workspace, size_t workspace_bytes,
+                               dust_stream_t s_, const dust_event_t* stage_events) {
+  if (!logits || !targets || !X || !g_hat || !G_W) return DUST_ERR_INVALID_ARG;
+  if (!dtype_ok(logits_dt) || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || T > kMaxT || !width_ok(V) || d <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
+  if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
+  if (T * V > kMaxElems || T * d > kMaxElems || K * T > kMaxElems || V * d > kMaxElems)
+    return DUST_ERR_UNSUPPORTED;
+  const HeadPlan plan = head_plan(T, V, d, K, gamma);
+  if (workspace == nullptr || workspace_bytes < plan.total()) return DUST_ERR_WORKSPACE;
+
+  hipStream_t s = as_stream(s_);
+  char* ws = reinterpret_cast<char*>(aligned_base(workspace));
+  float* delta = reinterpret_cast<float*>(ws);
+  void* gemm_ws = ws + align_up(plan.delta_bytes);
+  const bool zbf16 = (logits_dt == DUST_BF16);
+
+  hipError_t e = record(stage_events, 0, s);
+  if (e != hipSuccess) return DUST_ERR_HIP;
+  if (plan.fused) {
+    e = dust::launch_head_fused(logits, zbf16, targets, T, V, sigma, K, stream, seed, g_hat,
+                                losses_opt, s);
+    if (e != hipSuccess) return DUST_ERR_HIP;
+    if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
+    if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
+  } else {
+    e = dust::launch_head_losses(logits, zbf16, targets, T, V, sigma, K, stream, seed,
+                                 losses_opt, delta, s);
+    if (e != hipSuccess) return DUST_ERR_HIP;
+    if ((e = dust::launch_centre(delta, K, T, delta, s)) != hipSuccess) return DUST_ERR_HIP;
+    if (gamma != 0.f &&
+        (e = dust::launch_reward_scan(delta, K, T, seq_len, gamma, delta, s)) != hipSuccess)
+      return DUST_ERR_HIP;
+    if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
+    e = dust::launch_error_estimate(delta, K, T, V, sigma, stream, seed, g_hat, s);
+    if (e != hipSuccess) return DUST_ERR_HIP;
+    if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
+  }
+  e = dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, V, d, G_W, gemm_ws, s);
+  if (e != hipSuccess) return DUST_ERR_HIP;
+  return hip_status(record(stage_events, 3, s));
+}
+
+dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c, int64_t T,
+                                 int64_t d_in, int64_t N, int64_t seq_len, float sigma, int64_t K,
+                                 float gamma, uint64_t seed, uint32_t stream, float* g_hat,
+                                 float* G_W, void* workspace, size_t workspace_bytes,
+                                 dust_stream_t s_, const dust_event_t* stage_events) {
+  if (!X || !c || !g_hat || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || T > kMaxT || !width_ok(N) || d_in <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
+  if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
+  if (T * N > kMaxElems || T * d_in > kMaxElems || K * T > kMaxElems || N * d_in > kMaxElems)
+    return DUST_ERR_UNSUPPORTED;
+  const LinearPlan plan = linear_plan(T, d_in, N, K, gamma);
+  if (workspace == nullptr || workspace_bytes < plan.total()) return DUST_ERR_WORKSPACE;
+
+  hipStream_t s = as_stream(s_);
+  char* ws = reinterpret_cast<char*>(aligned_base(workspace));
+  float* r = reinterpret_cast<float*>(ws);
+  void* gemm_ws = ws + align_up(plan.r_bytes);
+
+  hipError_t e = record(stage_events, 0, s);
+  if (e != hipSuccess) return DUST_ERR_HIP;
+  const float* rr = c;
+  if (gamma != 0.f) {
+    if ((e = dust::launch_reward_scan(c, K, T, seq_len, gamma, r, s)) != hipSuccess)
+      return DUST_ERR_HIP;
+    rr = r;
+  }
+  if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
+  if ((e = dust::launch_error_estimate(rr, K, T, N, sigma, stream, seed, g_hat, s)) != hipSuccess)
+    return DUST_ERR_HIP;
+  if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
+  if ((e = dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, N, d_in, G_W, gemm_ws, s)) !=
+      hipSuccess)
+    return DUST_ERR_HIP;
+  return hip_status(record(stage_events, 3, s));
+}
+
+dust_status dust_noise(uint64_t seed, uint32_t stream, int64_t draw0, int64_t ndraw, int64_t T,
+                       int64_t N, float* out, dust_stream_t s) {
+  if (!out || ndraw < 0 || T < 0 || !width_ok(N) || draw0 < 0) return DUST_ERR_INVALID_ARG;
+  if (draw0 + ndraw > ((int64_t)1 << 32) || T > ((int64_t)1 << 32)) return DUST_ERR_INVALID_ARG;
+  if (ndraw * T > kMaxElems / N) return DUST_ERR_UNSUPPORTED;
+  return hip_status(dust::launch_noise_fill(out, ndraw, T, N, (uint32_t)draw0, stream, seed,
+                                            as_stream(s)));
+}
+
+dust_status dust_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t n,
+                               dust_stream_t s) {
+  if (n < 0 || n > kMaxElems) return DUST_ERR_INVALID_ARG;
+  if (n > 0 && (!ctr || !out)) return DUST_ERR_INVALID_ARG;
+  return hip_status(dust::launch_philox_raw(ctr, out, n, seed, as_stream(s)));
+}
+
+dust_status dust_head_losses(const void* logits, dust_dtype logits_dt, const int32_t* targets,
+                             int64_t T, int64_t V, float sigma, int64_t K, uint64_t seed,
+                             uint32_t stream, float* losses, dust_stream_t s) {
+  if (!logits || !targets || !losses || !dtype_ok(logits_dt)) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || T > kMaxT || !width_ok(V) || K <= 0 || K > kMaxK || !sigma_ok(sigma))
+    return DUST_ERR_INVALID_ARG;
+  if (T * V > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  return hip_status(dust::launch_head_losses(logits, logits_dt == DUST_BF16, targets, T, V, sigma,
+                                             K, stream, seed, losses, nullptr, as_stream(s)));
+}
+
+dust_status dust_centre(const float* x, int64_t K, int64_t T, float* c, dust_stream_t s) {
+  if (!x || !c || K <= 0 || T <= 0 || K * T > kMaxElems) return DUST_ERR_INVALID_ARG;
+  return hip_status(dust::launch_centre(x, K, T, c, as_stream(s)));
+}
+
+dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_len, float gamma,
+                             float* r, dust_stream_t s) {
+  if (!c || !r || K <= 0 || T <= 0 || K * T > kMaxElems) return DUST_ERR_INVALID_ARG;
+  if (seq_len <= 0 || T % seq_len != 0 || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
+  return hip_status(dust::launch_reward_scan(c, K, T, seq_len, gamma, r, as_stream(s)));
+}
+
+dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
+                                uint64_t seed, uint32_t stream, float* g_hat, dust_stream_t s) {
+  if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || T > kMaxT || !width_ok(N) ||
+      !sigma_ok(sigma))
+    return DUST_ERR_INVALID_ARG;
+  if (T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  return hip_status(
+      dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, g_hat, as_stream(s)));
+}
+
+dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, int64_t T,
+                           int64_t N, int64_t d, float* G_W, void* workspace,
+                           size_t workspace_bytes, dust_stream_t s) {
+  if (!g_hat || !X || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || T > kMaxT || N <= 0 || d <= 0) return DUST_ERR_INVALID_ARG;
+  if (T * N > kMaxElems || T * d > kMaxElems || N * d > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < dust_outer_sum_workspace_size(T, N, d))
+    return DUST_ERR_WORKSPACE;
+  return hip_status(dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, N, d, G_W,
+                                           aligned_base(workspace), as_stream(s)));
+}
+
+dust_status dust_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
+                               dust_stream_t s_) {
+  if (!targets || !flag || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(s_);
+  if (dust::launch_check_targets(targets, T, V, flag, s) != hipSuccess) return DUST_ERR_HIP;
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return DUST_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DUST_ERR_HIP;
+  return h ? DUST_ERR_TARGETS : DUST_OK;
+}
+
+}  // extern "C"

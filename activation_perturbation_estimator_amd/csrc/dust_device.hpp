@@ -1,0 +1,120 @@
+// dust_device.hpp -- device building blocks shared by the libdust kernels:
+// the counter-based noise generator and wavefront reductions (gfx950, wave64).
+//
+// Noise: the pages (laoyaoba analysis, mechanism section; linlog explainer,
+// "the core of Dust") ask for a_t ~ N(0, I), independent per token and per
+// draw.  libdust draws it from Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC'11) followed by Box-Muller
+// (Box & Muller, 1958), so that any element can be recomputed from its
+// coordinates (draw, token, column) instead of being stored.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dust {
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;  // golden ratio
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;  // sqrt(3) - 1
+
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+// Philox4x32 with 10 rounds.  Each round multiplies counter words 0 and 2 by
+// the two multipliers (full 64-bit products), xors the high halves with the
+// other two counter words and the round key, keeps the low halves, and bumps
+// the key by the Weyl increments.  Words that are the same in every lane
+// (token, draw, stream, key) stay in scalar registers, so the first two rounds
+// cost one vector product each instead of two.
+__device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                          uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// u = ((x >> 9) + 1/2) * 2^-23, exactly.  The 23 top bits are placed under the
+// exponent of 1.0f, giving 1 + m 2^-23 in [1, 2); subtracting 1 - 2^-24 is
+// exact (Sterbenz) and yields m 2^-23 + 2^-24 in (0, 1).
+__device__ __forceinline__ float unit_open(uint32_t x) {
+  const uint32_t bits = __builtin_amdgcn_alignbit(0x7Fu, x, 9u);  // (x >> 9) | 0x3F800000
+  return __uint_as_float(bits) - 0.999999940395355224609375f;
+}
+
+// Four standard normals from one Philox block, Box-Muller on (u0,u1) and
+// (u2,u3): radius sqrt(-2 ln u_even), angle 2 pi u_odd, cosine first.
+// v_log_f32 is log2, v_sin_f32 / v_cos_f32 take the angle in revolutions.
+__device__ __forceinline__ void box_muller4(const u32x4& x, float& a0, float& a1, float& a2,
+                                            float& a3) {
+  constexpr float kMinus2Ln2 = -1.38629436111989061883f;
+  const float u0 = unit_open(x.x), u1 = unit_open(x.y);
+  const float u2 = unit_open(x.z), u3 = unit_open(x.w);
+  const float r0 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(u0));
+  const float r1 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(u2));
+  a0 = r0 * __builtin_amdgcn_cosf(u1);
+  a1 = r0 * __builtin_amdgcn_sinf(u1);
+  a2 = r1 * __builtin_amdgcn_cosf(u3);
+  a3 = r1 * __builtin_amdgcn_sinf(u3);
+}
+
+// The four normals of columns 4j .. 4j+3 of a^(draw)_token.
+__device__ __forceinline__ void normal4(uint32_t j, uint32_t token, uint32_t draw,
+                                        uint32_t stream, uint32_t k0, uint32_t k1,
+                                        float& a0, float& a1, float& a2, float& a3) {
+  box_muller4(philox10(j, token, draw, stream, k0, k1), a0, a1, a2, a3);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront (64-lane) reductions.  DPP steps inside rows of 16 lanes, then the
+// four row sums combined in a fixed order, so the result is deterministic and
+// identical in every lane.
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+}  // namespace dust

@@ -1,0 +1,321 @@
+// dust_head.hip -- LM-head stages of the Dust estimator.
+//
+// The pages (laoyaoba analysis, mechanism section; linlog explainer, "the core
+// of Dust"; paper digest, section 2.3) perturb the LM head directly on the
+// cached logits and recompute only the per-token cross-entropy, which makes a
+// draw far cheaper than a forward pass.  For token t and draw i:
+//     l^(i)_t = logsumexp_v(z_tv + sigma a^(i)_tv) - (z_t,y + sigma a^(i)_t,y).
+//
+// One workgroup owns one token; each of its W waves owns an interleaved share of
+// the vocabulary (Philox block j = columns 4j..4j+3 goes to lane j mod 64W), and
+// the draws run in a loop.  The token's logits are read from HBM once, shifted
+// by the clean row maximum M and scaled by log2(e) into ztilde, and kept in LDS
+// for all K draws (in HBM/L2 for vocabularies too large for LDS).  A draw then
+// costs, per column, one Philox share, one Box-Muller share, one FMA, one exp2
+// and one add; the exp2 sum is reduced across the wave with DPP.
+//
+// Numerics: with S_i = sum_v 2^(ztilde_v + sigma log2(e) a_v) and S_0 the clean
+// sum, the loss change is delta_i = l_i - l_0 = ln(S_i / S_0) - sigma a_y.  It is
+// formed from the ratio, never as a difference of two ~log(V)-sized losses.
+//
+// Two variants share the code:
+//   kFused = false: writes delta_i (and optionally l_i) to [K,T] arrays; the
+//                   centring, gamma scan and error estimate run afterwards.
+//   kFused = true : gamma = 0 only.  The token's reward is its own centred
+//                   decrease c_i = dbar - delta_i (paper digest, section 2.2:
+//                   "gamma = 0: only itself"), so
+//                   sum_i c_i a_i = dbar sum_i a_i - sum_i delta_i a_i,
+//                   and the kernel keeps the draw's noise in registers until
+//                   delta_i is known, accumulates sum a and sum delta a, and
+//                   writes g_t = (sum delta a - dbar sum a) / (K sigma) once.
+//                   The noise is generated exactly once per (draw, token, column).
+#include "dust_device.hpp"
+#include "dust_launch.hpp"
+
+namespace dust {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename ZT>
+__device__ __forceinline__ void load4(const ZT* p, float& a, float& b, float& c, float& d);
+
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float& a, float& b, float& c,
+                                             float& d) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  a = v.x; b = v.y; c = v.z; d = v.w;
+}
+
+// bf16 -> fp32 is exact: the 16 bits become the high half of the fp32 word.
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float& a, float& b, float& c,
+                                                float& d) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  a = __uint_as_float(v.x << 16);
+  b = __uint_as_float(v.x & 0xFFFF0000u);
+  c = __uint_as_float(v.y << 16);
+  d = __uint_as_float(v.y & 0xFFFF0000u);
+}
+
+// Workgroup-wide sum / max of one value per wave (wave results already uniform).
+// `red` holds 2*W floats; `slot` alternates so that back-to-back reductions
+// need one barrier each.
+template <int W>
+__device__ __forceinline__ float group_sum(float wave_val, float* red, int slot) {
+  if constexpr (W == 1) {
+    return wave_val;
+  } else {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[slot * W + w] = wave_val;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < W; ++q) s += red[slot * W + q];
+    return s;
+  }
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float wave_val, float* red, int slot) {
+  if constexpr (W == 1) {
+    return wave_val;
+  } else {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[slot * W + w] = wave_val;
+    __syncthreads();
+    float s = red[slot * W];
+#pragma unroll
+    for (int q = 1; q < W; ++q) s = fmaxf(s, red[slot * W + q]);
+    return s;
+  }
+}
+
+// kNB: Philox blocks per lane per draw (4 kNB columns per lane).
+// kW : waves per token.  kW <= 4 keeps ztilde in LDS; larger vocabularies
+//      re-read the raw logits from global memory (L2-resident) every draw.
+template <int kNB, int kW, bool kFused, typename ZT>
+__global__ void __launch_bounds__(64 * kW)
+head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, int64_t T,
+            int64_t V, float sigma, int64_t K, uint32_t stream, uint32_t k0, uint32_t k1,
+            float* __restrict__ g_hat, float* __restrict__ losses, float* __restrict__ delta_out) {
+  constexpr bool kZInLds = (kW <= 4);
+  constexpr int kCols = 4 * kNB;
+  extern __shared__ float smem[];
+  float* red = smem;             // 2 * kW floats (padded to 64)
+  float* zs = smem + 64;         // kNB * 64 * kW * 4 floats when kZInLds
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  const int64_t nblk = V >> 2;
+  const ZT* zrow = logits + t * V;
+
+  // --- clean row: maximum, shifted/scaled logits, clean exp2 sum ----------
+  float zt[kCols];  // ztilde of this lane's columns (dead after staging when in LDS)
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const int64_t j = (int64_t)b * 64 * kW + wave * 64 + lane;
+    if (j < nblk) {
+      load4<ZT>(zrow + 4 * j, zt[4 * b], zt[4 * b + 1], zt[4 * b + 2], zt[4 * b + 3]);
+      mloc = fmaxf(mloc, fmaxf(fmaxf(zt[4 * b], zt[4 * b + 1]), fmaxf(zt[4 * b + 2], zt[4 * b + 3])));
+    } else {
+      zt[4 * b] = zt[4 * b + 1] = zt[4 * b + 2] = zt[4 * b + 3] = -INFINITY;
+    }
+  }
+  const float M = group_max<kW>(wave_max(mloc), red, 0);
+  const float Ml2e = M * kLog2e;
+  float s0 = 0.f;
+#pragma unroll
+  for (int q = 0; q < kCols; ++q) {
+    zt[q] = fmaf(zt[q], kLog2e, -Ml2e);  // -inf stays -inf (exp2 -> 0)
+    s0 += __builtin_amdgcn_exp2f(zt[q]);
+  }
+  if constexpr (kZInLds) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int j = b * 64 * kW + wave * 64 + lane;
+      *reinterpret_cast<float4*>(zs + 4 * j) =
+          make_float4(zt[4 * b], zt[4 * b + 1], zt[4 * b + 2], zt[4 * b + 3]);
+    }
+  }
+  const float S0 = group_sum<kW>(wave_sum(s0), red, 1);
+  const float inv_S0 = 1.0f / S0;
+  // An out-of-range target is clamped: the values are then meaningless, but
+  // every access stays inside the logits row.
+  const int32_t y = min(max(targets[t], 0), (int32_t)(V - 1));
+  float zy;
+  {
+    float c0, c1, c2, c3;
+    load4<ZT>(zrow + 4 * (y >> 2), c0, c1, c2, c3);
+    const int q = y & 3;
+    zy = q == 0 ? c0 : (q == 1 ? c1 : (q == 2 ? c2 : c3));
+  }
+  const float zty = fmaf(zy, kLog2e, -Ml2e);  // ztilde of the target column
+  const float ell0 = kLn2 * (__builtin_amdgcn_logf(S0) - zty);
+  if constexpr (kZInLds) __syncthreads();
+
+  const float sl2e = sigma * kLog2e;
+  float acc_a[kFused ? kCols : 1];
+  float acc_da[kFused ? kCols : 1];
+  if constexpr (kFused) {
+#pragma unroll
+    for (int q = 0; q < kCols; ++q) { acc_a[q] = 0.f; acc_da[q] = 0.f; }
+  }
+  float sum_delta = 0.f;
+  float ay_vec = 0.f;  // lane l: target-column noise of draw (i0 + l)
+
+  for (int64_t i = 0; i < K; ++i) {
+    const int il = (int)(i & 63);
+    if (il == 0) {
+      float a0, a1, a2, a3;
+      normal4((uint32_t)(y >> 2), (uint32_t)t, (uint32_t)(i + lane), stream, k0, k1, a0, a1, a2,
+              a3);
+      const int q = y & 3;
+      ay_vec = q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
+    }
+    float a[kCols];
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int j = b * 64 * kW + wave * 64 + lane;
+      normal4((uint32_t)j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a[4 * b], a[4 * b + 1],
+              a[4 * b + 2], a[4 * b + 3]);
+      float z0, z1, z2, z3;
+      if constexpr (kZInLds) {
+        const float4 zz = *reinterpret_cast<const float4*>(zs + 4 * j);
+        z0 = zz.x; z1 = zz.y; z2 = zz.z; z3 = zz.w;
+      } else {
+        if (j < nblk) {
+          load4<ZT>(zrow + 4 * (int64_t)j, z0, z1, z2, z3);
+          z0 = fmaf(z0, kLog2e, -Ml2e); z1 = fmaf(z1, kLog2e, -Ml2e);
+          z2 = fmaf(z2, kLog2e, -Ml2e); z3 = fmaf(z3, kLog2e, -Ml2e);
+        } else {
+          z0 = z1 = z2 = z3 = -INFINITY;
+        }
+      }
+      p0 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b], z0));
+      p1 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 1], z1));
+      p2 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 2], z2));
+      p3 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 3], z3));
+    }
+    const float Si = group_sum<kW>(wave_sum((p0 + p1) + (p2 + p3)), red, (int)(i & 1));
+    const float ay = lane_value(ay_vec, il);
+    const float delta = kLn2 * __builtin_amdgcn_logf(Si * inv_S0) - sigma * ay;
+    if constexpr (kFused) {
+      sum_delta += delta;
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) {
+        acc_a[q] += a[q];
+        acc_da[q] = fmaf(delta, a[q], acc_da[q]);
+      }
+    } else {
+      if (delta_out != nullptr && threadIdx.x == 0) delta_out[i * T + t] = delta;
+    }
+    if (losses != nullptr && threadIdx.x == 0) losses[i * T + t] = ell0 + delta;
+  }
+
+  if constexpr (kFused) {
+    const float dbar = sum_delta / (float)K;
+    const float scale = 1.0f / ((float)K * sigma);
+    float* grow = g_hat + t * V;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const int64_t j = (int64_t)b * 64 * kW + wave * 64 + lane;
+      if (j < nblk) {
+        float4 o;
+        o.x = (acc_da[4 * b] - dbar * acc_a[4 * b]) * scale;
+        o.y = (acc_da[4 * b + 1] - dbar * acc_a[4 * b + 1]) * scale;
+        o.z = (acc_da[4 * b + 2] - dbar * acc_a[4 * b + 2]) * scale;
+        o.w = (acc_da[4 * b + 3] - dbar * acc_a[4 * b + 3]) * scale;
+        *reinterpret_cast<float4*>(grow + 4 * j) = o;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Host-side launch configuration.
+// --------------------------------------------------------------------------
+HeadShape head_shape(int64_t V) {
+  const int64_t nblk = V / 4;
+  HeadShape h;
+  if (nblk <= 64) { h.nb = 1; h.w = 1; }
+  else if (nblk <= 128) { h.nb = 2; h.w = 1; }
+  else if (nblk <= 256) { h.nb = 4; h.w = 1; }
+  else if (nblk <= 512) { h.nb = 8; h.w = 1; }
+  else {
+    h.nb = 16;
+    const int64_t w = (nblk + 1023) / 1024;
+    h.w = w <= 1 ? 1 : w <= 2 ? 2 : w <= 4 ? 4 : w <= 8 ? 8 : 16;
+  }
+  return h;
+}
+
+bool head_fused_supported(int64_t V) {
+  // The fused kernel holds 12 values per column in registers; with more than
+  // 8 waves per workgroup they no longer fit.
+  return head_shape(V).w <= 8;
+}
+
+template <int kNB, int kW, bool kFused, typename ZT>
+static hipError_t launch_head_t(const void* logits, const int32_t* targets, int64_t T, int64_t V,
+                                float sigma, int64_t K, uint32_t stream, uint64_t seed,
+                                float* g_hat, float* losses, float* delta, hipStream_t s) {
+  constexpr bool kZInLds = (kW <= 4);
+  const size_t lds = sizeof(float) * (64 + (kZInLds ? (size_t)kNB * 64 * kW * 4 : 0));
+  hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT>), dim3((uint32_t)T), dim3(64 * kW), lds, s,
+                     reinterpret_cast<const ZT*>(logits), targets, T, V, sigma, K, stream,
+                     (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, losses, delta);
+  return hipGetLastError();
+}
+
+template <bool kFused, typename ZT>
+static hipError_t launch_head_dispatch(const void* logits, const int32_t* targets, int64_t T,
+                                       int64_t V, float sigma, int64_t K, uint32_t stream,
+                                       uint64_t seed, float* g_hat, float* losses, float* delta,
+                                       hipStream_t s) {
+  const HeadShape h = head_shape(V);
+#define DUST_HEAD_CASE(NB, W)                                                                   \
+  if (h.nb == NB && h.w == W)                                                                   \
+    return launch_head_t<NB, W, kFused, ZT>(logits, targets, T, V, sigma, K, stream, seed, g_hat, \
+                                            losses, delta, s);
+  DUST_HEAD_CASE(1, 1)
+  DUST_HEAD_CASE(2, 1)
+  DUST_HEAD_CASE(4, 1)
+  DUST_HEAD_CASE(8, 1)
+  DUST_HEAD_CASE(16, 1)
+  DUST_HEAD_CASE(16, 2)
+  DUST_HEAD_CASE(16, 4)
+  DUST_HEAD_CASE(16, 8)
+  if constexpr (!kFused) {
+    DUST_HEAD_CASE(16, 16)
+  }
+#undef DUST_HEAD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_fused(const void* logits, bool logits_bf16, const int32_t* targets,
+                             int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
+                             uint64_t seed, float* g_hat, float* losses, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  return logits_bf16
+             ? launch_head_dispatch<true, uint16_t>(logits, targets, T, V, sigma, K, stream, seed,
+                                                    g_hat, losses, nullptr, s)
+             : launch_head_dispatch<true, float>(logits, targets, T, V, sigma, K, stream, seed,
+                                                 g_hat, losses, nullptr, s);
+}
+
+hipError_t launch_head_losses(const void* logits, bool logits_bf16, const int32_t* targets,
+                              int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
+                              uint64_t seed, float* losses, float* delta, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  return logits_bf16
+             ? launch_head_dispatch<false, uint16_t>(logits, targets, T, V, sigma, K, stream, seed,
+                                                     nullptr, losses, delta, s)
+             : launch_head_dispatch<false, float>(logits, targets, T, V, sigma, K, stream, seed,
+                                                  nullptr, losses, delta, s);
+}
+
+}  // namespace dust

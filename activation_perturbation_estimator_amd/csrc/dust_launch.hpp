@@ -1,0 +1,51 @@
+// dust_launch.hpp -- internal host-side launchers of the libdust kernels.
+// Sizes have been validated by the C ABI layer before any of these is called;
+// each returns the HIP status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dust {
+
+// Noise stage.
+hipError_t launch_philox_raw(const uint32_t* ctr, uint32_t* out, int64_t n, uint64_t seed,
+                             hipStream_t s);
+hipError_t launch_noise_fill(float* out, int64_t ndraw, int64_t T, int64_t N, uint32_t draw0,
+                             uint32_t stream, uint64_t seed, hipStream_t s);
+
+// LM head.  Work split: one workgroup of 64*w threads per token, nb Philox
+// blocks per lane per draw.
+struct HeadShape {
+  int nb;
+  int w;
+};
+HeadShape head_shape(int64_t V);
+bool head_fused_supported(int64_t V);
+hipError_t launch_head_fused(const void* logits, bool logits_bf16, const int32_t* targets,
+                             int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
+                             uint64_t seed, float* g_hat, float* losses, hipStream_t s);
+hipError_t launch_head_losses(const void* logits, bool logits_bf16, const int32_t* targets,
+                              int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
+                              uint64_t seed, float* losses, float* delta, hipStream_t s);
+
+// Centring and the discounted-reward scan.
+hipError_t launch_centre(const float* x, int64_t K, int64_t T, float* c, hipStream_t s);
+hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, float gamma,
+                              float* r, hipStream_t s);
+
+// Error estimate from rewards with regenerated noise.
+hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
+                                 uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s);
+
+// Outer-product sum G = g^T X on the matrix cores.
+size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d);
+hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
+                            int64_t d, float* G, void* workspace, hipStream_t s);
+
+// Target range check; flag must be a device int32.
+hipError_t launch_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
+                                hipStream_t s);
+
+}  // namespace dust

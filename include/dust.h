@@ -1,0 +1,207 @@
+/*
+ * dust.h -- C ABI of libdust, the MI355X (gfx950) implementation of the Dust
+ * virtual-population gradient estimator.
+ *
+ * The method ("Dust: Pretraining Transformers Without Backpropagation",
+ * Q Labs), as the pages about it describe it:
+ *   - HN-mirror digest of the paper, section 2.1 (activation-space
+ *     perturbation) and section 2.2 (credit assignment): a linear layer's
+ *     output y_t = W x_t is jittered to y_t + sigma a_t, independently for every
+ *     token; token s scores a draw by its centred loss decrease c_s; the reward
+ *     is r_t = sum_{s>=t} gamma^(s-t) c_s (gamma = 0: the token's own c); over K
+ *     draws the output-error estimate is g_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i)
+ *     and the weight gradient is G_W = sum_t g_t x_t^T.
+ *   - laoyaoba analysis, mechanism section, and linlog explainer, section "the
+ *     core of Dust: virtual population": a_t ~ N(0, I); the LM head is perturbed
+ *     directly on the cached logits and only the cross-entropy is recomputed.
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device pointers are HIP device memory owned by the
+ *     caller.  The library allocates nothing and keeps no state between calls,
+ *     so calls on different streams may run concurrently (they must not share
+ *     output or workspace buffers).
+ *   - Calls enqueue kernels on the caller's stream `s` and return without
+ *     waiting, except dust_check_targets, which waits for its own result.
+ *     Outputs are overwritten, never accumulated.
+ *   - All argument checks run on the host before any HIP call; a rejected call
+ *     has no effect.  Launch failures are reported as DUST_ERR_HIP.  Nothing is
+ *     thrown across this interface.
+ *   - Layouts are row-major; [A,B] means A rows of B contiguous elements.
+ *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens),
+ *     N = layer output width (N = V for the LM head, N % 4 == 0), d = layer
+ *     input width, K draws.
+ *
+ * Noise convention (the pages fix only "standard normal, independent per
+ * token"; this library's counter-based stream, reproduced by
+ * dust_noise):  a^(i)_t[n] for draw i, token t, column n comes from the
+ * Philox4x32-10 block (Salmon et al., SC'11) with key (seed mod 2^32,
+ * seed >> 32) and counter words (n / 4, t, i, stream).  Each 32-bit output word
+ * x becomes u = ((x >> 9) + 1/2) * 2^-23, and Box-Muller maps (u0,u1) to
+ * columns 4j, 4j+1 (radius sqrt(-2 ln u0), angle 2 pi u1, cosine first) and
+ * (u2,u3) to columns 4j+2, 4j+3.  Draw indices and token indices are 0-based
+ * within the call.
+ */
+#ifndef DUST_H
+#define DUST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DUST_OK = 0,
+    DUST_ERR_INVALID_ARG = 1, /* null pointer, bad size or parameter            */
+    DUST_ERR_WORKSPACE = 2,   /* workspace pointer null or smaller than needed    */
+    DUST_ERR_HIP = 3,         /* a HIP launch or runtime call failed              */
+    DUST_ERR_UNSUPPORTED = 4, /* valid request this build cannot serve (size)     */
+    DUST_ERR_TARGETS = 5      /* dust_check_targets found a target out of range   */
+} dust_status;
+
+typedef enum { DUST_F32 = 0, DUST_BF16 = 1 } dust_dtype;
+
+/* Opaque stream and event handles: a hipStream_t / hipEvent_t cast to void*.
+ * A null stream is HIP's default stream. */
+typedef void* dust_stream_t;
+typedef void* dust_event_t;
+
+/* Largest accepted sigma.  The LM-head kernels take the exponentials relative
+ * to the clean row maximum; |sigma a| <= 8 * 5.77 keeps every term of the
+ * perturbed sum inside fp32 range. */
+#define DUST_SIGMA_MAX 8.0f
+/* Largest accepted vocabulary / layer width N. */
+#define DUST_N_MAX 65536
+/* Number of stage events dust_head_estimate / dust_linear_estimate record
+ * when `stage_events` is non-null (see below). */
+#define DUST_STAGE_EVENTS 4
+
+/* Human-readable name of a status code (static string, never null). */
+const char* dust_status_string(dust_status st);
+
+/* Library version string, e.g. "libdust 1.0 gfx950". */
+const char* dust_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Composed estimators                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* LM head (laoyaoba analysis, mechanism section; linlog explainer, "the core
+ * of Dust"; paper digest, sections 2.2-2.3): noise on the cached logits, the
+ * per-token cross-entropy recomputed for every draw, then centring, the
+ * gamma scan, the error estimate and the outer product of the paper digest,
+ * section 2.2.
+ *   logits  device [T,V], dtype logits_dt (DUST_F32 or DUST_BF16), read only
+ *   targets device [T] int32, 0 <= targets[t] < V (not checked here: see
+ *           dust_check_targets; an out-of-range target gives undefined values,
+ *           never an out-of-bounds access)
+ *   X       device [T,d], dtype x_dt, the head's input activations
+ *   sigma   noise scale, 0 < sigma <= DUST_SIGMA_MAX
+ *   K       draws, 1 <= K < 2^31 (K = 1 gives g_hat = 0: centring zeroes c)
+ *   gamma   discount, 0 <= gamma <= 1; the scan restarts at every sequence
+ *   seed, stream   noise key and fourth counter word
+ *   g_hat   device [T,V] fp32 out: the output-error estimate g_t
+ *   G_W     device [V,d] fp32 out: sum_t g_t x_t^T (a sum over tokens)
+ *   losses_opt  device [K,T] fp32 out (per-draw perturbed losses) or NULL
+ *   workspace   device scratch of at least dust_head_workspace_size(...) bytes
+ *   stage_events  NULL, or DUST_STAGE_EVENTS events recorded on s: [0] before
+ *           the first kernel, [1] after the per-draw loss / fused estimate
+ *           stage, [2] after the error-estimate stage, [3] after the outer
+ *           product.  Stages a call skips record back to back.
+ * Requires V % 4 == 0, V <= DUST_N_MAX, T % seq_len == 0. */
+dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt,
+                               const int32_t* targets,
+                               const void* X, dust_dtype x_dt,
+                               int64_t T, int64_t V, int64_t d, int64_t seq_len,
+                               float sigma, int64_t K, float gamma,
+                               uint64_t seed, uint32_t stream,
+                               float* g_hat, float* G_W, float* losses_opt,
+                               void* workspace, size_t workspace_bytes,
+                               dust_stream_t s, const dust_event_t* stage_events);
+
+/* Bytes of workspace dust_head_estimate needs (0 is never returned). */
+size_t dust_head_workspace_size(int64_t T, int64_t V, int64_t d, int64_t K, float gamma);
+
+/* Hidden linear layer y = W x (paper digest, section 2.2): the caller ran its
+ * K perturbed forwards with noise from dust_noise(seed, stream, 0, K, T, N)
+ * and measured c[i,t], the centred loss decrease of token t under draw i.  c
+ * is used as given (the library does not centre it).
+ *   X      device [T,d_in], dtype x_dt
+ *   c      device [K,T] fp32
+ *   g_hat  device [T,N] fp32 out;  G_W device [N,d_in] fp32 out
+ * Same rules as above for sigma, K, gamma, seq_len, N % 4, workspace and
+ * stage_events ([1] after the gamma scan). */
+dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
+                                 int64_t T, int64_t d_in, int64_t N, int64_t seq_len,
+                                 float sigma, int64_t K, float gamma,
+                                 uint64_t seed, uint32_t stream,
+                                 float* g_hat, float* G_W,
+                                 void* workspace, size_t workspace_bytes,
+                                 dust_stream_t s, const dust_event_t* stage_events);
+
+size_t dust_linear_workspace_size(int64_t T, int64_t d_in, int64_t N, int64_t K, float gamma);
+
+/* ------------------------------------------------------------------------ */
+/* Stages (each is one step of the estimator and can be called on its own)   */
+/* ------------------------------------------------------------------------ */
+
+/* Noise (laoyaoba analysis, mechanism section; paper digest, section 2.1):
+ * out[k,t,n] = a^(draw0+k)_t[n] for k < ndraw, t < T, n < N (N % 4 == 0).
+ * For a caller's perturbed forward y + sigma a and for tests.
+ *   out device [ndraw,T,N] fp32. */
+dust_status dust_noise(uint64_t seed, uint32_t stream, int64_t draw0, int64_t ndraw,
+                       int64_t T, int64_t N, float* out, dust_stream_t s);
+
+/* Raw Philox4x32-10 blocks: out[b] = Philox(key = seed, counter = ctr[b]).
+ *   ctr, out device [n,4] uint32.  n may be 0. */
+dust_status dust_philox4x32_10(uint64_t seed, const uint32_t* ctr, uint32_t* out, int64_t n,
+                               dust_stream_t s);
+
+/* Per-draw LM-head losses (laoyaoba analysis, mechanism section; linlog
+ * explainer): losses[i,t] = CE(logits_t + sigma a^(i)_t, targets[t]) in nats.
+ *   losses device [K,T] fp32 out. */
+dust_status dust_head_losses(const void* logits, dust_dtype logits_dt, const int32_t* targets,
+                             int64_t T, int64_t V, float sigma, int64_t K,
+                             uint64_t seed, uint32_t stream, float* losses, dust_stream_t s);
+
+/* Centring (paper digest, section 2.2, "centred loss decrease"):
+ * c[i,t] = mean_j x[j,t] - x[i,t] for per-draw losses x [K,T]; this is the
+ * loss decrease d_i = l0 - l_i minus its mean over the draws, whatever the
+ * clean loss l0.  x and c device [K,T] fp32; c may equal x (in place). */
+dust_status dust_centre(const float* x, int64_t K, int64_t T, float* c, dust_stream_t s);
+
+/* Discounted reward (paper digest, section 2.2):
+ * r[i,t] = c[i,t] + gamma r[i,t+1] inside each sequence of seq_len tokens,
+ * r = c at a sequence's last token.  c, r device [K,T] fp32; r may equal c. */
+dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_len,
+                             float gamma, float* r, dust_stream_t s);
+
+/* Error estimate (paper digest, section 2.2):
+ * g_hat[t,n] = -(1/(K sigma)) sum_i r[i,t] a^(i)_t[n], the noise regenerated
+ * from (seed, stream).  r device [K,T] fp32; g_hat device [T,N] fp32 out. */
+dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N,
+                                float sigma, uint64_t seed, uint32_t stream,
+                                float* g_hat, dust_stream_t s);
+
+/* Weight gradient (paper digest, section 2.2): G_W[n,k] = sum_t g_hat[t,n] X[t,k].
+ *   g_hat device [T,N] fp32; X device [T,d], dtype x_dt; G_W device [N,d] fp32
+ *   out; workspace of at least dust_outer_sum_workspace_size(T,N,d) bytes.
+ * N need not be a multiple of 4 here. */
+dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt,
+                           int64_t T, int64_t N, int64_t d, float* G_W,
+                           void* workspace, size_t workspace_bytes, dust_stream_t s);
+
+size_t dust_outer_sum_workspace_size(int64_t T, int64_t N, int64_t d);
+
+/* Checks 0 <= targets[t] < V for all t; waits on s for the answer.
+ * Returns DUST_OK or DUST_ERR_TARGETS.  `flag` is a device int32 the call
+ * overwrites (caller-owned scratch). */
+dust_status dust_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
+                               dust_stream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUST_H */
