@@ -4,7 +4,7 @@
 // gives the output-error estimate
 //     g_t = -(1/(K sigma)) sum_i r^(i)_t a^(i)_t .
 // The noise a^(i)_t is never read from memory: each lane regenerates its
-// columns' Philox blocks from (column/4, token, draw, stream), so the kernel
+// columns' Philox blocks from (token, column/4, draw, stream), so the kernel
 // moves only r (4 bytes per token-draw) and g (4 bytes per token-column).
 //
 // One workgroup per token (W waves split the columns as in the head kernels);
@@ -69,7 +69,7 @@ hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N
                                  uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const float scale = -1.0f / ((float)K * sigma);
-  const HeadShape h = head_shape(N);
+  const HeadShape h = wide_shape(N);
 #define DUST_EE_CASE(NB, W) \
   if (h.nb == NB && h.w == W) return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, g_hat, s);
   DUST_EE_CASE(1, 1)

@@ -8,7 +8,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/dust.h"
+#include "dust.h"
 #include "dust_launch.hpp"
 
 namespace {

@@ -23,27 +23,58 @@ struct u32x4 {
   uint32_t x, y, z, w;
 };
 
-// Philox4x32 with 10 rounds.  Each round multiplies counter words 0 and 2 by
-// the two multipliers (full 64-bit products), xors the high halves with the
-// other two counter words and the round key, keeps the low halves, and bumps
-// the key by the Weyl increments.  Words that are the same in every lane
-// (token, draw, stream, key) stay in scalar registers, so the first two rounds
-// cost one vector product each instead of two.
+// Three-input xor in one gfx950 instruction (v_bitop3_b32, truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
+// One Philox4x32 round: counter words 0 and 2 are multiplied by the two
+// multipliers (full 64-bit products); the high halves are xor-ed with the other
+// two counter words and the round key; the low halves are kept.
+template <bool kBitop3>
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                             uint32_t& c3, uint32_t k0, uint32_t k1) {
+  const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
+  const uint64_t p1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
+  uint32_t n0, n2;
+  if constexpr (kBitop3) {
+    n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+  } else {
+    n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+  }
+  c1 = (uint32_t)p1;
+  c3 = (uint32_t)p0;
+  c0 = n0;
+  c2 = n2;
+}
+
+// Philox4x32-10 on an arbitrary counter: 10 rounds, the key bumped by the Weyl
+// increments between rounds.
 __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                           uint32_t k0, uint32_t k1) {
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
-    const uint64_t p1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-    c1 = (uint32_t)p1;
-    c3 = (uint32_t)p0;
-    c0 = n0;
-    c2 = n2;
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
+  for (int r = 0; r < 10; ++r)
+    philox_round<true>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The same function for the counters of a noise row, (token, column/4, draw,
+// stream), where only the column word differs between lanes.  The column enters
+// through a xor, so the first rounds are mostly lane-uniform: their uniform
+// parts run on the scalar unit (plain xors let the compiler split them off),
+// and the vector work is 16 products instead of 20.  From the fourth round on
+// every word differs between lanes and each three-input xor is one bitop3.
+__device__ __forceinline__ u32x4 philox10_row(uint32_t token, uint32_t j, uint32_t draw,
+                                              uint32_t stream, uint32_t k0, uint32_t k1) {
+  uint32_t c0 = token, c1 = j, c2 = draw, c3 = stream;
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    philox_round<false>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+#pragma unroll
+  for (int r = 3; r < 10; ++r)
+    philox_round<true>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
   return u32x4{c0, c1, c2, c3};
 }
 
@@ -75,7 +106,7 @@ __device__ __forceinline__ void box_muller4(const u32x4& x, float& a0, float& a1
 __device__ __forceinline__ void normal4(uint32_t j, uint32_t token, uint32_t draw,
                                         uint32_t stream, uint32_t k0, uint32_t k1,
                                         float& a0, float& a1, float& a2, float& a3) {
-  box_muller4(philox10(j, token, draw, stream, k0, k1), a0, a1, a2, a3);
+  box_muller4(philox10_row(token, j, draw, stream, k0, k1), a0, a1, a2, a3);
 }
 
 // ---------------------------------------------------------------------------

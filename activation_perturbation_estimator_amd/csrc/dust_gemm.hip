@@ -11,15 +11,17 @@
 // fp32 accumulation: g_hi X + g_lo X for bf16 X (exact in bf16), plus
 // g_hi X_lo for fp32 X.  Every bf16 x bf16 product is exact in fp32.
 //
-// Tiling: a workgroup (4 waves) owns a 128 x 128 tile of G over one token range
-// (split-K over tokens so that the grid fills the 256 CUs).  Per 32-token step
-// the fp32 g tile is read with each lane walking 8 tokens of one column (every
-// load instruction reads 64 consecutive floats), split to hi/lo and written to
-// LDS transposed (token-contiguous), which is the operand layout of
+// Layout: both operands are needed token-contiguous (the operand layout of
 // v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and the 8 consecutive
-// contraction indices 8*(l/32) .. 8*(l/32)+7.  Each wave computes 64 x 64 of
-// the tile as 2 x 2 MFMA blocks.  Partial tiles of the token splits are summed
-// in a fixed order by a second kernel, so results are deterministic.
+// contraction indices 8*(l/32) .. 8*(l/32)+7).  X is small and read by every
+// tile, so a prologue transposes it once to Xt [d][T] bf16.  g is large and read
+// once: each lane walks 8 tokens of one column (every load instruction reads 64
+// consecutive floats), splits to hi/lo and writes 16-byte rows to LDS.
+//
+// Tiling: a workgroup (4 waves) owns a 128 x 256 tile of G over one token range
+// (split-K over tokens so that the grid fills the 256 CUs), double-buffered in
+// LDS.  Partial tiles of the token splits are summed in a fixed order by a
+// second kernel, so results are deterministic.
 #include "dust_device.hpp"
 #include "dust_launch.hpp"
 
@@ -27,212 +29,313 @@ namespace dust {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
-constexpr int kBM = 128;      // rows of G (layer outputs) per workgroup
-constexpr int kBN = 128;      // columns of G (layer inputs) per workgroup
-constexpr int kBT = 32;       // tokens per step
-constexpr int kLdsRow = kBT + 8;  // bf16 per LDS row (80 bytes: 16-byte aligned, staggered banks)
+constexpr int kBM = 128;          // rows of G (layer outputs) per workgroup
+constexpr int kBN = 256;          // columns of G (layer inputs) per workgroup
+constexpr int kBT = 32;           // tokens per pipeline step
+constexpr int kRow = kBT + 8;     // bf16 per LDS row: 80 bytes, 16-byte aligned
+constexpr int kXcds = 8;          // MI355X: workgroups go round-robin to 8 XCDs
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 values -> packed bf16 hi and packed bf16 lo (v_cvt_pk_bf16_f32, round
+// to nearest even): v = hi + lo + O(2^-17 |v|).
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2_t v = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  const f32x2_t r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
 }
 
-__device__ __forceinline__ void split_bf16(float v, uint32_t& hi, uint32_t& lo) {
-  hi = bf16_bits(v);
-  const float rest = v - __uint_as_float(hi << 16);  // exact
-  lo = bf16_bits(rest);
-}
-
+// X [T,d] -> Xt [d][Tp] bf16 (token-contiguous, zero beyond T), and for fp32 X
+// its hi/lo split.  32 x 32 tiles through LDS: coalesced reads along d,
+// coalesced writes along tokens.
 template <bool kXF32>
-__global__ void __launch_bounds__(256)
-outer_sum_kernel(const float* __restrict__ g, const void* __restrict__ Xv, int64_t T, int64_t M,
-                 int64_t Nd, int64_t t_per_split, float* __restrict__ out, int64_t split_stride) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bh[kBN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bl[kXF32 ? kBN * kLdsRow : 8];
+__global__ void __launch_bounds__(256) x_transpose_kernel(const void* __restrict__ Xv, int64_t T,
+                                                          int64_t d, int64_t Tp,
+                                                          uint16_t* __restrict__ xt_hi,
+                                                          uint16_t* __restrict__ xt_lo) {
+  __shared__ float tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  const int64_t t0 = (int64_t)blockIdx.x * 32, n0 = (int64_t)blockIdx.y * 32;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = t0 + ty + 8 * k, n = n0 + tx;
+    float v = 0.f;
+    if (t < T && n < d) {
+      if constexpr (kXF32) v = reinterpret_cast<const float*>(Xv)[t * d + n];
+      else v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + n] << 16);
+    }
+    tile[ty + 8 * k][tx] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t n = n0 + ty + 8 * k, t = t0 + tx;
+    if (n < d && t < Tp) {
+      const float v = tile[tx][ty + 8 * k];
+      if constexpr (kXF32) {
+        uint32_t hi, lo;
+        split2(v, 0.f, hi, lo);
+        xt_hi[n * Tp + t] = (uint16_t)hi;
+        xt_lo[n * Tp + t] = (uint16_t)lo;
+      } else {
+        xt_hi[n * Tp + t] = (uint16_t)(__float_as_uint(v) >> 16);
+      }
+    }
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+struct GemmGeom {
+  int64_t M, Nd, T, Tp, tiles_m, tiles_n, nsplit, t_per_split, groups, groups_per_xcd;
+};
+
+// Main kernel.  Workgroup = 4 waves on a 128 x 256 tile of G for one token
+// split; each wave owns 64 x 128 as 2 x 4 MFMA blocks.  Tokens advance 32 at a
+// time through two LDS stages: the next step's g and Xt are fetched into
+// registers while the matrix cores work on the current stage.
+template <bool kXF32>
+__global__ void __launch_bounds__(256, kXF32 ? 1 : 2)
+outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi,
+                 const uint16_t* __restrict__ xt_lo, GemmGeom geo, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  constexpr int kA = kBM * kRow, kB = kBN * kRow;
+  constexpr int kStage = 2 * kA + (kXF32 ? 2 : 1) * kB;
+
+  // XCD-aware order: the tiles_n workgroups that share one (m tile, split) are
+  // consecutive on the same XCD, so the second reads g from that XCD's L2.
+  const int64_t id = blockIdx.x;
+  const int64_t xcd = id % kXcds, rank = id / kXcds;
+  const int64_t group = (rank / geo.tiles_n) * kXcds + xcd;
+  if (group >= geo.groups) return;  // padding workgroup: leaves before any barrier
+  const int64_t ntile = rank % geo.tiles_n;
+  const int64_t mtile = group % geo.tiles_m, split = group / geo.tiles_m;
+  const int64_t m0 = mtile * kBM, n0 = ntile * kBN;
+  const int64_t t_begin = split * geo.t_per_split;
+  const int64_t t_end = min(geo.T, t_begin + geo.t_per_split);
+  const int nsteps = (int)((t_end - t_begin + kBT - 1) / kBT);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t m0 = (blockIdx.x % tiles_m) * kBM;
-  const int64_t n0 = (blockIdx.x / tiles_m) * kBN;
-  const int64_t t_begin = (int64_t)blockIdx.y * t_per_split;
-  int64_t t_end = t_begin + t_per_split;
-  if (t_end > T) t_end = T;
+  const int arow = tid & 127, aq = tid >> 7;  // A staging: row, token groups aq and aq + 2
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int row = tid & 127;    // staging: this thread's row of the A / B tile
-  const int qbase = tid >> 7;   // token groups qbase and qbase + 2 (8 tokens each)
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kBT) {
-    // ---- stage g (A operand), transposed to token-contiguous rows ----
+  float av[16];
+  uint4 bh[4], bl[kXF32 ? 4 : 1];
+  auto fetch = [&](int64_t t0) {
+    const int64_t m = m0 + arow;
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = qbase + 2 * qq;
-      const int64_t m = m0 + row;
-      uint32_t hi[8], lo[8];
+    for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t tt = t0 + 8 * q + e;
-        const float v = (tt < t_end && m < M) ? g[tt * M + m] : 0.f;
-        split_bf16(v, hi[e], lo[e]);
+        const int64_t t = t0 + 8 * (aq + 2 * qq) + e;
+        av[8 * qq + e] = (t < t_end && m < geo.M) ? g[t * geo.M + m] : 0.f;
       }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int chunk = tid + 256 * k;
+      const int64_t n = n0 + (chunk >> 2);
+      const int64_t off = n * geo.Tp + t0 + 8 * (chunk & 3);
+      if (n < geo.Nd) {
+        bh[k] = *reinterpret_cast<const uint4*>(xt_hi + off);
+        if constexpr (kXF32) bl[k] = *reinterpret_cast<const uint4*>(xt_lo + off);
+      } else {
+        bh[k] = make_uint4(0, 0, 0, 0);
+        if constexpr (kXF32) bl[k] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stash = [&](int stage) {
+    uint16_t* base = lds + stage * kStage;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
       uint4 ph, pl;
-      ph.x = hi[0] | (hi[1] << 16); ph.y = hi[2] | (hi[3] << 16);
-      ph.z = hi[4] | (hi[5] << 16); ph.w = hi[6] | (hi[7] << 16);
-      pl.x = lo[0] | (lo[1] << 16); pl.y = lo[2] | (lo[3] << 16);
-      pl.z = lo[4] | (lo[5] << 16); pl.w = lo[6] | (lo[7] << 16);
-      *reinterpret_cast<uint4*>(&Ah[row * kLdsRow + 8 * q]) = ph;
-      *reinterpret_cast<uint4*>(&Al[row * kLdsRow + 8 * q]) = pl;
+      split2(av[8 * qq + 0], av[8 * qq + 1], ph.x, pl.x);
+      split2(av[8 * qq + 2], av[8 * qq + 3], ph.y, pl.y);
+      split2(av[8 * qq + 4], av[8 * qq + 5], ph.z, pl.z);
+      split2(av[8 * qq + 6], av[8 * qq + 7], ph.w, pl.w);
+      const int off = arow * kRow + 8 * (aq + 2 * qq);
+      *reinterpret_cast<uint4*>(base + off) = ph;
+      *reinterpret_cast<uint4*>(base + kA + off) = pl;
     }
-    // ---- stage X (B operand) ----
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int q = qbase + 2 * qq;
-      const int64_t n = n0 + row;
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t tt = t0 + 8 * q + e;
-        const bool ok = (tt < t_end && n < Nd);
-        if constexpr (kXF32) {
-          const float v = ok ? reinterpret_cast<const float*>(Xv)[tt * Nd + n] : 0.f;
-          split_bf16(v, hi[e], lo[e]);
-        } else {
-          hi[e] = ok ? (uint32_t)reinterpret_cast<const uint16_t*>(Xv)[tt * Nd + n] : 0u;
-          lo[e] = 0u;
-        }
-      }
-      uint4 ph;
-      ph.x = hi[0] | (hi[1] << 16); ph.y = hi[2] | (hi[3] << 16);
-      ph.z = hi[4] | (hi[5] << 16); ph.w = hi[6] | (hi[7] << 16);
-      *reinterpret_cast<uint4*>(&Bh[row * kLdsRow + 8 * q]) = ph;
-      if constexpr (kXF32) {
-        uint4 pl;
-        pl.x = lo[0] | (lo[1] << 16); pl.y = lo[2] | (lo[3] << 16);
-        pl.z = lo[4] | (lo[5] << 16); pl.w = lo[6] | (lo[7] << 16);
-        *reinterpret_cast<uint4*>(&Bl[row * kLdsRow + 8 * q]) = pl;
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int chunk = tid + 256 * k;
+      const int off = (chunk >> 2) * kRow + 8 * (chunk & 3);
+      *reinterpret_cast<uint4*>(base + 2 * kA + off) = bh[k];
+      if constexpr (kXF32) *reinterpret_cast<uint4*>(base + 2 * kA + kB + off) = bl[k];
     }
-    __syncthreads();
+  };
 
+  if (nsteps > 0) {
+    fetch(t_begin);
+    stash(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = (s + 1 < nsteps);
+    if (more) fetch(t_begin + (int64_t)(s + 1) * kBT);
+    const uint16_t* base = lds + (s & 1) * kStage;
 #pragma unroll
     for (int kk = 0; kk < kBT; kk += 16) {
       const int koff = kk + 8 * (lane >> 5);
-      bf16x8_t ah[2], al[2], bh[2], bl[2];
+      bf16x8_t fah[2], fal[2], fbh[4], fbl[kXF32 ? 4 : 1];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int r = wm * 64 + mb * 32 + (lane & 31);
-        ah[mb] = *reinterpret_cast<const bf16x8_t*>(&Ah[r * kLdsRow + koff]);
-        al[mb] = *reinterpret_cast<const bf16x8_t*>(&Al[r * kLdsRow + koff]);
+        fah[mb] = *reinterpret_cast<const bf16x8_t*>(base + r * kRow + koff);
+        fal[mb] = *reinterpret_cast<const bf16x8_t*>(base + kA + r * kRow + koff);
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int r = wn * 64 + nb * 32 + (lane & 31);
-        bh[nb] = *reinterpret_cast<const bf16x8_t*>(&Bh[r * kLdsRow + koff]);
-        if constexpr (kXF32) bl[nb] = *reinterpret_cast<const bf16x8_t*>(&Bl[r * kLdsRow + koff]);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int r = wn * 128 + nb * 32 + (lane & 31);
+        fbh[nb] = *reinterpret_cast<const bf16x8_t*>(base + 2 * kA + r * kRow + koff);
+        if constexpr (kXF32)
+          fbl[nb] = *reinterpret_cast<const bf16x8_t*>(base + 2 * kA + kB + r * kRow + koff);
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < 4; ++nb) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fah[mb], fbh[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fal[mb], fbh[nb], acc[mb][nb], 0, 0, 0);
           if constexpr (kXF32)
-            acc[mb][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fah[mb], fbl[nb], acc[mb][nb], 0, 0, 0);
         }
     }
+    if (more) stash((s + 1) & 1);
     __syncthreads();
   }
 
-  // ---- write the 64 x 64 wave tile: register r of block (mb, nb) holds
-  // row 8*(r/4) + 4*(lane/32) + r%4, column lane%32 ----
-  float* o = out + (int64_t)blockIdx.y * split_stride;
+  // Register r of block (mb, nb) holds row 8*(r/4) + 4*(lane/32) + r%4 and
+  // column lane%32 of that 32 x 32 block.
+  float* o = out + split * geo.M * geo.Nd;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = n0 + wn * 64 + nb * 32 + (lane & 31);
-        if (m < M && n < Nd) o[m * Nd + n] = acc[mb][nb][r];
+        const int64_t n = n0 + wn * 128 + nb * 32 + (lane & 31);
+        if (m < geo.M && n < geo.Nd) o[m * geo.Nd + n] = acc[mb][nb][r];
       }
 }
 
-// G[e] = sum_s part[s][e] in split order.
+// G[e] = sum_s part[s][e] in split order (four elements per thread).
 __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part,
                                                            int64_t nsplit, int64_t n,
                                                            float* __restrict__ G) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+  const int64_t n4 = n / 4;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += stride) {
+    float4 s = reinterpret_cast<const float4*>(part)[e];
+    for (int64_t q = 1; q < nsplit; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(part + q * n)[e];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    reinterpret_cast<float4*>(G)[e] = s;
+  }
+  for (int64_t e = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
     float s = part[e];
     for (int64_t q = 1; q < nsplit; ++q) s += part[q * n + e];
     G[e] = s;
   }
 }
 
-struct SplitPlan {
-  int64_t tiles;
-  int64_t nsplit;
-  int64_t t_per_split;
-};
-
-static SplitPlan plan_splits(int64_t T, int64_t M, int64_t Nd) {
-  SplitPlan p;
-  p.tiles = ((M + kBM - 1) / kBM) * ((Nd + kBN - 1) / kBN);
-  // Aim for >= 1024 workgroups (4 per CU) with >= 512 tokens per split.
-  int64_t want = (1024 + p.tiles - 1) / p.tiles;
+static GemmGeom plan(int64_t T, int64_t M, int64_t Nd) {
+  GemmGeom g;
+  g.M = M;
+  g.Nd = Nd;
+  g.T = T;
+  g.Tp = (T + kBT - 1) / kBT * kBT;
+  if (g.Tp == 0) g.Tp = kBT;
+  g.tiles_m = (M + kBM - 1) / kBM;
+  g.tiles_n = (Nd + kBN - 1) / kBN;
+  const int64_t tiles = g.tiles_m * g.tiles_n;
+  // Aim for >= 512 workgroups (2 per CU) with >= 512 tokens per split.
+  int64_t want = (512 + tiles - 1) / tiles;
   int64_t cap = (T + 511) / 512;
   if (cap < 1) cap = 1;
-  p.nsplit = want < cap ? want : cap;
-  if (p.nsplit < 1) p.nsplit = 1;
-  int64_t per = (T + p.nsplit - 1) / p.nsplit;
+  int64_t ns = want < cap ? want : cap;
+  if (ns < 1) ns = 1;
+  int64_t per = (T + ns - 1) / ns;
   per = (per + kBT - 1) / kBT * kBT;
-  p.t_per_split = per > 0 ? per : kBT;
-  p.nsplit = (T + p.t_per_split - 1) / p.t_per_split;
-  if (p.nsplit < 1) p.nsplit = 1;
-  return p;
+  g.t_per_split = per > 0 ? per : kBT;
+  g.nsplit = (T + g.t_per_split - 1) / g.t_per_split;
+  if (g.nsplit < 1) g.nsplit = 1;
+  g.groups = g.tiles_m * g.nsplit;
+  g.groups_per_xcd = (g.groups + kXcds - 1) / kXcds;
+  return g;
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace: Xt_hi [d][Tp] bf16, Xt_lo (fp32 X only), split partials [S][N][d] fp32.
+static void ws_layout(const GemmGeom& g, bool x_f32, size_t& xt_bytes, size_t& part_bytes) {
+  xt_bytes = align256((size_t)g.Nd * (size_t)g.Tp * 2);
+  part_bytes = g.nsplit > 1 ? (size_t)g.nsplit * (size_t)g.M * (size_t)g.Nd * sizeof(float) : 0;
+  (void)x_f32;
 }
 
 size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d) {
-  const SplitPlan p = plan_splits(T, N, d);
-  if (p.nsplit <= 1) return 0;
-  return (size_t)p.nsplit * (size_t)N * (size_t)d * sizeof(float);
+  const GemmGeom g = plan(T, N, d);
+  size_t xt, part;
+  ws_layout(g, true, xt, part);
+  return 2 * xt + part;  // sized for fp32 X (hi and lo); bf16 X uses the first half
+}
+
+template <bool kXF32>
+static hipError_t launch_gemm_t(const GemmGeom& geo, const float* g, const uint16_t* xh,
+                                const uint16_t* xl, float* out, hipStream_t s) {
+  constexpr int kStageBytes = 2 * (2 * kBM * kRow + (kXF32 ? 2 : 1) * kBN * kRow);
+  const size_t lds = 2 * (size_t)kStageBytes;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&outer_sum_kernel<kXF32>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nwg = geo.groups_per_xcd * kXcds * geo.tiles_n;
+  hipLaunchKernelGGL(outer_sum_kernel<kXF32>, dim3((uint32_t)nwg), dim3(256), lds, s, g, xh, xl,
+                     geo, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
                             int64_t d, float* G, void* workspace, hipStream_t s) {
-  const SplitPlan p = plan_splits(T, N, d);
-  float* out = (p.nsplit > 1) ? reinterpret_cast<float*>(workspace) : G;
-  const int64_t split_stride = N * d;
-  dim3 grid((uint32_t)p.tiles, (uint32_t)p.nsplit);
+  const GemmGeom geo = plan(T, N, d);
+  size_t xt_bytes, part_bytes;
+  ws_layout(geo, !x_bf16, xt_bytes, part_bytes);
+  char* ws = reinterpret_cast<char*>(workspace);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(ws + xt_bytes);
+  float* part = reinterpret_cast<float*>(ws + 2 * xt_bytes);
+  float* out = (geo.nsplit > 1) ? part : G;
+
+  dim3 tgrid((uint32_t)(geo.Tp / 32), (uint32_t)((d + 31) / 32));
   if (x_bf16)
-    hipLaunchKernelGGL(outer_sum_kernel<false>, grid, dim3(256), 0, s, g, X, T, N, d,
-                       p.t_per_split, out, split_stride);
+    hipLaunchKernelGGL(x_transpose_kernel<false>, tgrid, dim3(256), 0, s, X, T, d, geo.Tp, xh,
+                       nullptr);
   else
-    hipLaunchKernelGGL(outer_sum_kernel<true>, grid, dim3(256), 0, s, g, X, T, N, d,
-                       p.t_per_split, out, split_stride);
+    hipLaunchKernelGGL(x_transpose_kernel<true>, tgrid, dim3(256), 0, s, X, T, d, geo.Tp, xh, xl);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit <= 1) return e;
+  if (e != hipSuccess) return e;
+  e = x_bf16 ? launch_gemm_t<false>(geo, g, xh, nullptr, out, s)
+             : launch_gemm_t<true>(geo, g, xh, xl, out, s);
+  if (e != hipSuccess || geo.nsplit <= 1) return e;
   const int64_t n = N * d;
-  int64_t blocks = (n + 255) / 256;
+  int64_t blocks = (n / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, out, p.nsplit,
-                     n, G);
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, part,
+                     geo.nsplit, n, G);
   return hipGetLastError();
 }
 

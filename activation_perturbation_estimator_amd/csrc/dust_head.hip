@@ -91,15 +91,15 @@ __device__ __forceinline__ float group_max(float wave_val, float* red, int slot)
   }
 }
 
-// kNB: Philox blocks per lane per draw (4 kNB columns per lane).
-// kW : waves per token.  kW <= 4 keeps ztilde in LDS; larger vocabularies
-//      re-read the raw logits from global memory (L2-resident) every draw.
-template <int kNB, int kW, bool kFused, typename ZT>
+// kNB    : Philox blocks per lane per draw (4 kNB columns per lane).
+// kW     : waves per token.
+// kZInLds: ztilde staged in LDS (V <= 32768); wider vocabularies re-read the
+//          raw logits from global memory (L2-resident) every draw.
+template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds>
 __global__ void __launch_bounds__(64 * kW)
 head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, int64_t T,
             int64_t V, float sigma, int64_t K, uint32_t stream, uint32_t k0, uint32_t k1,
             float* __restrict__ g_hat, float* __restrict__ losses, float* __restrict__ delta_out) {
-  constexpr bool kZInLds = (kW <= 4);
   constexpr int kCols = 4 * kNB;
   extern __shared__ float smem[];
   float* red = smem;             // 2 * kW floats (padded to 64)
@@ -238,7 +238,29 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
 // --------------------------------------------------------------------------
 // Host-side launch configuration.
 // --------------------------------------------------------------------------
-HeadShape head_shape(int64_t V) {
+constexpr int64_t kLdsVocabMax = 32768;  // ztilde (4 bytes per column) fits LDS
+
+// Fused kernel: 16 columns per lane and up to 16 waves per token, which keeps a
+// lane's draw noise and both accumulators near 100 VGPRs (4 waves per SIMD).
+// Wider rows use 64 columns per lane on 8 waves.
+HeadShape fused_shape(int64_t V) {
+  const int64_t nblk = V / 4;
+  HeadShape h;
+  if (nblk <= 64) { h.nb = 1; h.w = 1; }
+  else if (nblk <= 128) { h.nb = 2; h.w = 1; }
+  else if (nblk <= 256) { h.nb = 4; h.w = 1; }
+  else if (nblk <= 512) { h.nb = 4; h.w = 2; }
+  else if (nblk <= 1024) { h.nb = 4; h.w = 4; }
+  else if (nblk <= 2048) { h.nb = 4; h.w = 8; }
+  else if (nblk <= 4096) { h.nb = 4; h.w = 16; }
+  else if (nblk <= 8192) { h.nb = 16; h.w = 8; }
+  else { h.nb = 0; h.w = 0; }
+  return h;
+}
+
+// Kernels that keep at most one value per column (per-draw losses, error
+// estimate): up to 64 columns per lane on one wave, then more waves.
+HeadShape wide_shape(int64_t V) {
   const int64_t nblk = V / 4;
   HeadShape h;
   if (nblk <= 64) { h.nb = 1; h.w = 1; }
@@ -253,20 +275,21 @@ HeadShape head_shape(int64_t V) {
   return h;
 }
 
-bool head_fused_supported(int64_t V) {
-  // The fused kernel holds 12 values per column in registers; with more than
-  // 8 waves per workgroup they no longer fit.
-  return head_shape(V).w <= 8;
-}
+bool head_fused_supported(int64_t V) { return fused_shape(V).nb != 0; }
 
-template <int kNB, int kW, bool kFused, typename ZT>
+template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds>
 static hipError_t launch_head_t(const void* logits, const int32_t* targets, int64_t T, int64_t V,
                                 float sigma, int64_t K, uint32_t stream, uint64_t seed,
                                 float* g_hat, float* losses, float* delta, hipStream_t s) {
-  constexpr bool kZInLds = (kW <= 4);
   const size_t lds = sizeof(float) * (64 + (kZInLds ? (size_t)kNB * 64 * kW * 4 : 0));
-  hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT>), dim3((uint32_t)T), dim3(64 * kW), lds, s,
-                     reinterpret_cast<const ZT*>(logits), targets, T, V, sigma, K, stream,
+  if (lds > 65536) {  // above the default dynamic-LDS limit: raise it for this kernel
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&head_kernel<kNB, kW, kFused, ZT, kZInLds>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT, kZInLds>), dim3((uint32_t)T), dim3(64 * kW),
+                     lds, s, reinterpret_cast<const ZT*>(logits), targets, T, V, sigma, K, stream,
                      (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, losses, delta);
   return hipGetLastError();
 }
@@ -276,21 +299,28 @@ static hipError_t launch_head_dispatch(const void* logits, const int32_t* target
                                        int64_t V, float sigma, int64_t K, uint32_t stream,
                                        uint64_t seed, float* g_hat, float* losses, float* delta,
                                        hipStream_t s) {
-  const HeadShape h = head_shape(V);
-#define DUST_HEAD_CASE(NB, W)                                                                   \
-  if (h.nb == NB && h.w == W)                                                                   \
-    return launch_head_t<NB, W, kFused, ZT>(logits, targets, T, V, sigma, K, stream, seed, g_hat, \
-                                            losses, delta, s);
-  DUST_HEAD_CASE(1, 1)
-  DUST_HEAD_CASE(2, 1)
-  DUST_HEAD_CASE(4, 1)
-  DUST_HEAD_CASE(8, 1)
-  DUST_HEAD_CASE(16, 1)
-  DUST_HEAD_CASE(16, 2)
-  DUST_HEAD_CASE(16, 4)
-  DUST_HEAD_CASE(16, 8)
-  if constexpr (!kFused) {
-    DUST_HEAD_CASE(16, 16)
+  const HeadShape h = kFused ? fused_shape(V) : wide_shape(V);
+  const bool lds = V <= kLdsVocabMax;
+#define DUST_HEAD_CASE(NB, W, LDS)                                                              \
+  if (h.nb == NB && h.w == W && lds == LDS)                                                     \
+    return launch_head_t<NB, W, kFused, ZT, LDS>(logits, targets, T, V, sigma, K, stream, seed, \
+                                                 g_hat, losses, delta, s);
+  DUST_HEAD_CASE(1, 1, true)
+  DUST_HEAD_CASE(2, 1, true)
+  DUST_HEAD_CASE(4, 1, true)
+  if constexpr (kFused) {
+    DUST_HEAD_CASE(4, 2, true)
+    DUST_HEAD_CASE(4, 4, true)
+    DUST_HEAD_CASE(4, 8, true)
+    DUST_HEAD_CASE(4, 16, true)
+    DUST_HEAD_CASE(16, 8, true)
+  } else {
+    DUST_HEAD_CASE(8, 1, true)
+    DUST_HEAD_CASE(16, 1, true)
+    DUST_HEAD_CASE(16, 2, true)
+    DUST_HEAD_CASE(16, 4, true)
+    DUST_HEAD_CASE(16, 8, true)
+    DUST_HEAD_CASE(16, 16, false)
   }
 #undef DUST_HEAD_CASE
   return hipErrorInvalidValue;

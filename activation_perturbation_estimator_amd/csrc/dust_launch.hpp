@@ -21,7 +21,8 @@ struct HeadShape {
   int nb;
   int w;
 };
-HeadShape head_shape(int64_t V);
+HeadShape fused_shape(int64_t V);   // the fused gamma = 0 kernel (0 if unsupported)
+HeadShape wide_shape(int64_t V);    // per-draw losses and the error estimate
 bool head_fused_supported(int64_t V);
 hipError_t launch_head_fused(const void* logits, bool logits_bf16, const int32_t* targets,
                              int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,

@@ -35,7 +35,7 @@
  * token"; this library's counter-based stream, reproduced by
  * dust_noise):  a^(i)_t[n] for draw i, token t, column n comes from the
  * Philox4x32-10 block (Salmon et al., SC'11) with key (seed mod 2^32,
- * seed >> 32) and counter words (n / 4, t, i, stream).  Each 32-bit output word
+ * seed >> 32) and counter words (t, n / 4, i, stream).  Each 32-bit output word
  * x becomes u = ((x >> 9) + 1/2) * 2^-23, and Box-Muller maps (u0,u1) to
  * columns 4j, 4j+1 (radius sqrt(-2 ln u0), angle 2 pi u1, cosine first) and
  * (u2,u3) to columns 4j+2, 4j+3.  Draw indices and token indices are 0-based

@@ -23,7 +23,7 @@
  * Readings taken where the pages are silent (each listed in the design notes):
  *   - "centred" = subtract the per-token mean over the K draws.
  *   - noise stream = Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit
- *     seed, counter (column/4, token, draw, stream), mapped to uniforms in
+ *     seed, counter (token, column/4, draw, stream), mapped to uniforms in
  *     (0,1) by the top 23 bits, then Box-Muller (1958).
  *   - the gamma scan restarts at every sequence boundary (seq_len tokens).
  *   - G_W sums over tokens (no mean); no bias term.
@@ -89,7 +89,7 @@ void oracle_normal4(uint64_t seed, uint32_t j, uint32_t t, uint32_t i, uint32_t 
                     double a[4])
 {
     const double two_pi = 6.283185307179586476925286766559;
-    uint32_t ctr[4] = { j, t, i, stream };
+    uint32_t ctr[4] = { t, j, i, stream };
     uint32_t x[4];
     oracle_philox4x32_10(seed, ctr, x);
     double u0 = oracle_uniform(x[0]), u1 = oracle_uniform(x[1]);

@@ -94,7 +94,7 @@ def test_box_muller_inverts_to_the_block_uniforms():
     a = oracle.noise(seed, stream, 0, ndraw, T, N)
     for i in range(ndraw):
         for t in range(T):
-            ctr = np.array([[j, t, i, stream] for j in range(N // 4)], dtype=np.uint32)
+            ctr = np.array([[t, j, i, stream] for j in range(N // 4)], dtype=np.uint32)
             u = oracle.uniform(oracle.philox4x32_10(seed, ctr).ravel()).reshape(-1, 4)
             row = a[i, t].reshape(-1, 4)
             for p in (0, 1):
