@@ -23,8 +23,10 @@ bool sigma_ok(float sigma) {
 bool gamma_ok(float gamma) { return std::isfinite(gamma) && gamma >= 0.f && gamma <= 1.f; }
 bool dtype_ok(dust_dtype dt) { return dt == DUST_F32 || dt == DUST_BF16; }
 
-// Index products stay far below 2^62 and the 32-bit counter words hold t and i.
-constexpr int64_t kMaxT = (int64_t)1 << 31;
+// Index products stay far below 2^62, the 32-bit counter words hold t and i,
+// and the outer product's 32-bit buffer offsets cover 256 rows of X^T.
+constexpr int64_t kMaxT = (int64_t)1 << 22;          // calls that form G_W
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;     // calls that do not
 constexpr int64_t kMaxK = ((int64_t)1 << 31) - 64;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
@@ -117,7 +119,8 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
                                dust_stream_t s_, const dust_event_t* stage_events) {
   if (!logits || !targets || !X || !g_hat || !G_W) return DUST_ERR_INVALID_ARG;
   if (!dtype_ok(logits_dt) || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxT || !width_ok(V) || d <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || !width_ok(V) || d <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
   if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * V > kMaxElems || T * d > kMaxElems || K * T > kMaxElems || V * d > kMaxElems)
@@ -163,7 +166,8 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
                                  float* G_W, void* workspace, size_t workspace_bytes,
                                  dust_stream_t s_, const dust_event_t* stage_events) {
   if (!X || !c || !g_hat || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxT || !width_ok(N) || d_in <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || !width_ok(N) || d_in <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
   if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * N > kMaxElems || T * d_in > kMaxElems || K * T > kMaxElems || N * d_in > kMaxElems)
@@ -214,7 +218,7 @@ dust_status dust_head_losses(const void* logits, dust_dtype logits_dt, const int
                              int64_t T, int64_t V, float sigma, int64_t K, uint64_t seed,
                              uint32_t stream, float* losses, dust_stream_t s) {
   if (!logits || !targets || !losses || !dtype_ok(logits_dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxT || !width_ok(V) || K <= 0 || K > kMaxK || !sigma_ok(sigma))
+  if (T <= 0 || T > kMaxTokens || !width_ok(V) || K <= 0 || K > kMaxK || !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
   if (T * V > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_head_losses(logits, logits_dt == DUST_BF16, targets, T, V, sigma,
@@ -235,7 +239,7 @@ dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_l
 
 dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
                                 uint64_t seed, uint32_t stream, float* g_hat, dust_stream_t s) {
-  if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || T > kMaxT || !width_ok(N) ||
+  if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || T > kMaxTokens || !width_ok(N) ||
       !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
   if (T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
@@ -247,7 +251,8 @@ dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, i
                            int64_t N, int64_t d, float* G_W, void* workspace,
                            size_t workspace_bytes, dust_stream_t s) {
   if (!g_hat || !X || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxT || N <= 0 || d <= 0) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || N <= 0 || d <= 0) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
   if (T * N > kMaxElems || T * d > kMaxElems || N * d > kMaxElems) return DUST_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < dust_outer_sum_workspace_size(T, N, d))
     return DUST_ERR_WORKSPACE;

@@ -48,41 +48,53 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
 }
 
 // X [T,d] -> Xt [d][Tp] bf16 (token-contiguous, zero beyond T), and for fp32 X
-// its hi/lo split.  32 x 32 tiles through LDS: coalesced reads along d,
-// coalesced writes along tokens.
+// its hi/lo split.  64 x 64 tiles through LDS; every thread reads 4 consecutive
+// columns of one token and writes 4 consecutive tokens of one column.
 template <bool kXF32>
 __global__ void __launch_bounds__(256) x_transpose_kernel(const void* __restrict__ Xv, int64_t T,
                                                           int64_t d, int64_t Tp,
                                                           uint16_t* __restrict__ xt_hi,
                                                           uint16_t* __restrict__ xt_lo) {
-  __shared__ float tile[32][33];
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  const int64_t t0 = (int64_t)blockIdx.x * 32, n0 = (int64_t)blockIdx.y * 32;
+  __shared__ float tile[64][65];
+  const int64_t t0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 64;
+  const int c4 = (threadIdx.x & 15) * 4, r = threadIdx.x >> 4;  // 16 x 16 threads
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t t = t0 + ty + 8 * k, n = n0 + tx;
-    float v = 0.f;
-    if (t < T && n < d) {
-      if constexpr (kXF32) v = reinterpret_cast<const float*>(Xv)[t * d + n];
-      else v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + n] << 16);
+    const int tt = r + 16 * k;
+    const int64_t t = t0 + tt;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < T) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t n = n0 + c4 + e;
+        if (n < d) {
+          if constexpr (kXF32) v[e] = reinterpret_cast<const float*>(Xv)[t * d + n];
+          else v[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + n] << 16);
+        }
+      }
     }
-    tile[ty + 8 * k][tx] = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[tt][c4 + e] = v[e];
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t n = n0 + ty + 8 * k, t = t0 + tx;
-    if (n < d && t < Tp) {
-      const float v = tile[tx][ty + 8 * k];
-      if constexpr (kXF32) {
-        uint32_t hi, lo;
-        split2(v, 0.f, hi, lo);
-        xt_hi[n * Tp + t] = (uint16_t)hi;
-        xt_lo[n * Tp + t] = (uint16_t)lo;
-      } else {
-        xt_hi[n * Tp + t] = (uint16_t)(__float_as_uint(v) >> 16);
-      }
+    const int nn = r + 16 * k;
+    const int64_t n = n0 + nn;
+    const int64_t t = t0 + c4;
+    if (n >= d || t >= Tp) continue;
+    const float a = tile[c4][nn], b = tile[c4 + 1][nn], c = tile[c4 + 2][nn], e = tile[c4 + 3][nn];
+    uint2 hi;
+    if constexpr (kXF32) {
+      uint2 lo;
+      split2(a, b, hi.x, lo.x);
+      split2(c, e, hi.y, lo.y);
+      *reinterpret_cast<uint2*>(xt_lo + n * Tp + t) = lo;
+    } else {
+      hi.x = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+      hi.y = (__float_as_uint(c) >> 16) | (__float_as_uint(e) & 0xFFFF0000u);
     }
+    *reinterpret_cast<uint2*>(xt_hi + n * Tp + t) = hi;
   }
 }
 
@@ -127,28 +139,45 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
+  // Buffer loads: out-of-range offsets read as 0.  The g window of this split
+  // ends at min(split end, T), so the last partial step of the last split reads
+  // zeros; rows m >= M read the next token's values, which only reach
+  // accumulator rows that are never stored.
+  const int64_t t_rows = t_end - t_begin;
+  const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(g + t_begin * geo.M), 0, (int)(t_rows * geo.M * 4), 0x00020000);
+  const int64_t n_rows = min((int64_t)kBN, geo.Nd - n0);
+  const __amdgpu_buffer_rsrc_t xh_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xt_hi + n0 * geo.Tp), 0, (int)(n_rows * geo.Tp * 2), 0x00020000);
+  __amdgpu_buffer_rsrc_t xl_rsrc = xh_rsrc;
+  if constexpr (kXF32)
+    xl_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xt_lo + n0 * geo.Tp), 0,
+                                                (int)(n_rows * geo.Tp * 2), 0x00020000);
+  const int a_voff = (int)((m0 + arow) * 4);
+  const int a_tstride = (int)(geo.M * 4);
+
   float av[16];
   uint4 bh[4], bl[kXF32 ? 4 : 1];
   auto fetch = [&](int64_t t0) {
-    const int64_t m = m0 + arow;
+    const int tl = (int)(t0 - t_begin);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t t = t0 + 8 * (aq + 2 * qq) + e;
-        av[8 * qq + e] = (t < t_end && m < geo.M) ? g[t * geo.M + m] : 0.f;
+        const int tt = tl + 8 * (aq + 2 * qq) + e;
+        av[8 * qq + e] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(g_rsrc, a_voff + tt * a_tstride, 0, 0));
       }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int chunk = tid + 256 * k;
-      const int64_t n = n0 + (chunk >> 2);
-      const int64_t off = n * geo.Tp + t0 + 8 * (chunk & 3);
-      if (n < geo.Nd) {
-        bh[k] = *reinterpret_cast<const uint4*>(xt_hi + off);
-        if constexpr (kXF32) bl[k] = *reinterpret_cast<const uint4*>(xt_lo + off);
-      } else {
-        bh[k] = make_uint4(0, 0, 0, 0);
-        if constexpr (kXF32) bl[k] = make_uint4(0, 0, 0, 0);
+      const int off = (int)(((chunk >> 2) * geo.Tp + t0 + 8 * (chunk & 3)) * 2);
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xh_rsrc, off, 0, 0);
+      bh[k] = make_uint4(v.x, v.y, v.z, v.w);
+      if constexpr (kXF32) {
+        u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(xl_rsrc, off, 0, 0);
+        bl[k] = make_uint4(w.x, w.y, w.z, w.w);
       }
     }
   };
@@ -268,6 +297,10 @@ static GemmGeom plan(int64_t T, int64_t M, int64_t Nd) {
   if (ns < 1) ns = 1;
   int64_t per = (T + ns - 1) / ns;
   per = (per + kBT - 1) / kBT * kBT;
+  // 32-bit buffer offsets: one split's slice of g stays below 2^31 bytes.
+  const int64_t mm = M > 0 ? M : 1;
+  const int64_t per_max = ((((int64_t)1 << 31) - 1 - 4 * (mm + kBM)) / (4 * mm)) / kBT * kBT;
+  if (per > per_max) per = per_max > kBT ? per_max : kBT;
   g.t_per_split = per > 0 ? per : kBT;
   g.nsplit = (T + g.t_per_split - 1) / g.t_per_split;
   if (g.nsplit < 1) g.nsplit = 1;
@@ -319,7 +352,7 @@ hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t 
   float* part = reinterpret_cast<float*>(ws + 2 * xt_bytes);
   float* out = (geo.nsplit > 1) ? part : G;
 
-  dim3 tgrid((uint32_t)(geo.Tp / 32), (uint32_t)((d + 31) / 32));
+  dim3 tgrid((uint32_t)((geo.Tp + 63) / 64), (uint32_t)((d + 63) / 64));
   if (x_bf16)
     hipLaunchKernelGGL(x_transpose_kernel<false>, tgrid, dim3(256), 0, s, X, T, d, geo.Tp, xh,
                        nullptr);

@@ -91,19 +91,41 @@ __device__ __forceinline__ float group_max(float wave_val, float* red, int slot)
   }
 }
 
+// Workgroup sums of kN wave-uniform values at once (one barrier).  Slot `slot`
+// of a kStride-wide layout; alternating slots need no second barrier.
+template <int W, int kN, int kStride>
+__device__ __forceinline__ void group_sum_n(float* v, float* red, int slot) {
+  if constexpr (W > 1) {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int d = 0; d < kN; ++d) red[(slot * kStride + d) * W + w] = v[d];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < kN; ++d) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < W; ++q) s += red[(slot * kStride + d) * W + q];
+      v[d] = s;
+    }
+  }
+}
+
 // kNB    : Philox blocks per lane per draw (4 kNB columns per lane).
 // kW     : waves per token.
 // kZInLds: ztilde staged in LDS (V <= 32768); wider vocabularies re-read the
 //          raw logits from global memory (L2-resident) every draw.
-template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds>
+// kDraws : draws per loop iteration (they share one cross-wave reduction).
+template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds, int kDraws>
 __global__ void __launch_bounds__(64 * kW)
 head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, int64_t T,
             int64_t V, float sigma, int64_t K, uint32_t stream, uint32_t k0, uint32_t k1,
             float* __restrict__ g_hat, float* __restrict__ losses, float* __restrict__ delta_out) {
   constexpr int kCols = 4 * kNB;
   extern __shared__ float smem[];
-  float* red = smem;             // 2 * kW floats (padded to 64)
-  float* zs = smem + 64;         // kNB * 64 * kW * 4 floats when kZInLds
+  float* red = smem;             // reductions: 2 kW + 2 kDraws kW <= 128 floats
+  float* zs = smem + 128;        // kNB * 64 * kW * 4 floats when kZInLds
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -164,18 +186,12 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
     for (int q = 0; q < kCols; ++q) { acc_a[q] = 0.f; acc_da[q] = 0.f; }
   }
   float sum_delta = 0.f;
-  float ay_vec = 0.f;  // lane l: target-column noise of draw (i0 + l)
+  float ay_vec = 0.f;  // lane l: target-column noise of draw (i0 + l), i0 = i & ~63
+  float* red_loop = red + 2 * kW;  // the prologue's reductions used red[0, 2 kW)
 
-  for (int64_t i = 0; i < K; ++i) {
-    const int il = (int)(i & 63);
-    if (il == 0) {
-      float a0, a1, a2, a3;
-      normal4((uint32_t)(y >> 2), (uint32_t)t, (uint32_t)(i + lane), stream, k0, k1, a0, a1, a2,
-              a3);
-      const int q = y & 3;
-      ay_vec = q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
-    }
-    float a[kCols];
+  // Noise of draw i for this lane's columns, and the lane's share of
+  // S_i = sum_v 2^(ztilde_v + sigma log2(e) a_v).
+  auto draw_noise = [&](int64_t i, float* a) -> float {
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
@@ -200,8 +216,20 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
       p2 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 2], z2));
       p3 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 3], z3));
     }
-    const float Si = group_sum<kW>(wave_sum((p0 + p1) + (p2 + p3)), red, (int)(i & 1));
-    const float ay = lane_value(ay_vec, il);
+    return (p0 + p1) + (p2 + p3);
+  };
+  auto refresh_target_noise = [&](int64_t i) {
+    if ((i & 63) == 0) {
+      float a0, a1, a2, a3;
+      normal4((uint32_t)(y >> 2), (uint32_t)t, (uint32_t)(i + lane), stream, k0, k1, a0, a1, a2,
+              a3);
+      const int q = y & 3;
+      ay_vec = q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
+    }
+  };
+  // Loss change of draw i from its full sum S_i; accumulate or write it.
+  auto finish = [&](int64_t i, float Si, const float* a) {
+    const float ay = lane_value(ay_vec, (int)(i & 63));
     const float delta = kLn2 * __builtin_amdgcn_logf(Si * inv_S0) - sigma * ay;
     if constexpr (kFused) {
       sum_delta += delta;
@@ -214,6 +242,27 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
       if (delta_out != nullptr && threadIdx.x == 0) delta_out[i * T + t] = delta;
     }
     if (losses != nullptr && threadIdx.x == 0) losses[i * T + t] = ell0 + delta;
+  };
+
+  // kDraws draws per iteration share one cross-wave reduction (one barrier).
+  int64_t i = 0;
+  int parity = 0;
+  for (; i + kDraws <= K; i += kDraws, parity ^= 1) {
+    refresh_target_noise(i);
+    float a[kDraws][kCols];
+    float S[kDraws];
+#pragma unroll
+    for (int d = 0; d < kDraws; ++d) S[d] = wave_sum(draw_noise(i + d, a[d]));
+    group_sum_n<kW, kDraws, kDraws>(S, red_loop, parity);
+#pragma unroll
+    for (int d = 0; d < kDraws; ++d) finish(i + d, S[d], a[d]);
+  }
+  for (; i < K; ++i, parity ^= 1) {  // tail when kDraws does not divide K
+    refresh_target_noise(i);
+    float a[kCols];
+    float S[1] = {wave_sum(draw_noise(i, a))};
+    group_sum_n<kW, 1, kDraws>(S, red_loop, parity);
+    finish(i, S[0], a);
   }
 
   if constexpr (kFused) {
@@ -239,6 +288,10 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
 // Host-side launch configuration.
 // --------------------------------------------------------------------------
 constexpr int64_t kLdsVocabMax = 32768;  // ztilde (4 bytes per column) fits LDS
+// Draws per cross-wave reduction in the fused kernel.  Two draws per barrier
+// cost more registers (two noise rows live at once) than the barrier they
+// save: measured on MI355X at V=4096, one draw per reduction is faster.
+constexpr int fused_draws(int nb) { return nb > 0 ? 1 : 1; }
 
 // Fused kernel: 16 columns per lane and up to 16 waves per token, which keeps a
 // lane's draw noise and both accumulators near 100 VGPRs (4 waves per SIMD).
@@ -281,14 +334,16 @@ template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds>
 static hipError_t launch_head_t(const void* logits, const int32_t* targets, int64_t T, int64_t V,
                                 float sigma, int64_t K, uint32_t stream, uint64_t seed,
                                 float* g_hat, float* losses, float* delta, hipStream_t s) {
-  const size_t lds = sizeof(float) * (64 + (kZInLds ? (size_t)kNB * 64 * kW * 4 : 0));
+  constexpr int kDraws = kFused ? fused_draws(kNB) : 1;
+  const size_t lds = sizeof(float) * (128 + (kZInLds ? (size_t)kNB * 64 * kW * 4 : 0));
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it for this kernel
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&head_kernel<kNB, kW, kFused, ZT, kZInLds>),
+        reinterpret_cast<const void*>(&head_kernel<kNB, kW, kFused, ZT, kZInLds, kDraws>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT, kZInLds>), dim3((uint32_t)T), dim3(64 * kW),
+  hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT, kZInLds, kDraws>), dim3((uint32_t)T),
+                     dim3(64 * kW),
                      lds, s, reinterpret_cast<const ZT*>(logits), targets, T, V, sigma, K, stream,
                      (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, losses, delta);
   return hipGetLastError();

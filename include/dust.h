@@ -27,7 +27,8 @@
  *     has no effect.  Launch failures are reported as DUST_ERR_HIP.  Nothing is
  *     thrown across this interface.
  *   - Layouts are row-major; [A,B] means A rows of B contiguous elements.
- *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens),
+ *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens;
+ *     T <= 2^22 per call for the calls that form G_W, DUST_ERR_UNSUPPORTED above),
  *     N = layer output width (N = V for the LM head, N % 4 == 0), d = layer
  *     input width, K draws.
  *
