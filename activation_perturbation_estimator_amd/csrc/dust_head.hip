@@ -21,9 +21,9 @@
 // Two variants share the code:
 //   kFused = false: writes delta_i (and optionally l_i) to [K,T] arrays; the
 //                   centring, gamma scan and error estimate run afterwards.
-//   kFused = true : gamma = 0 only.  The token's reward is its own centred
-//                   decrease c_i = dbar - delta_i (paper digest, section 2.2:
-//                   "gamma = 0: only itself"), so
+//   kFused = true : gamma = 0 only.  The token's reward is then its own
+//                   centred decrease c_i = dbar - delta_i (paper digest,
+//                   section 2.2), so
 //                   sum_i c_i a_i = dbar sum_i a_i - sum_i delta_i a_i,
 //                   and the kernel keeps the draw's noise in registers until
 //                   delta_i is known, accumulates sum a and sum delta a, and
@@ -291,7 +291,7 @@ constexpr int64_t kLdsVocabMax = 32768;  // ztilde (4 bytes per column) fits LDS
 // Draws per cross-wave reduction in the fused kernel.  Two draws per barrier
 // cost more registers (two noise rows live at once) than the barrier they
 // save: measured on MI355X at V=4096, one draw per reduction is faster.
-constexpr int fused_draws(int nb) { return nb > 0 ? 1 : 1; }
+constexpr int fused_draws(int /*nb*/) { return 1; }
 
 // Fused kernel: 16 columns per lane and up to 16 waves per token, which keeps a
 // lane's draw noise and both accumulators near 100 VGPRs (4 waves per SIMD).

@@ -1,6 +1,7 @@
 // dust_noise.hip -- the noise stage: raw Philox blocks and materialised
-// standard-normal noise a^(i)_t[n] (laoyaoba analysis, mechanism section:
-// "y -> y + sigma a with a standard normal, independently per token").
+// standard-normal noise a^(i)_t[n] (laoyaoba analysis, mechanism section: each
+// linear output is jittered by sigma times standard-normal noise, token by
+// token).
 //
 // The estimator kernels never read noise from memory: they regenerate it from
 // its counters.  These two kernels serve callers that apply the noise in their

@@ -6,7 +6,7 @@
 //     r_t = sum_{s >= t} gamma^(s-t) c_s          (gamma = 0: the token's own c).
 // The sum runs inside one sequence: causal attention cannot carry a token's
 // perturbation into another sequence, so the scan restarts at every sequence
-// boundary.  "Centred" is read as: subtract the mean over the K draws of the
+// boundary.  Centring is read as: subtract the mean over the K draws of the
 // same token.
 #include "dust_device.hpp"
 #include "dust_launch.hpp"

@@ -10,6 +10,7 @@ call's stream inside the timed loop) and the fp64 CPU oracle's rate on a
 bounded sample of the same workload.
 
   python bench.py [--steps 10] [--warmup 2] [--workload paper] [--no-cpu-baseline]
+                  [--copy-probe-mib 256]
 """
 from __future__ import annotations
 
@@ -24,23 +25,61 @@ sys.path.insert(0, ROOT)
 
 METRIC = "token-draws/sec, LM-head Dust estimator (T=16384, V=4096) + % VALU/MFMA peak"
 
-# MI355X published figures: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz issue
-# 39.3e12 non-packed 32-bit VALU lane-operations per second; bf16 dense MFMA
-# 2.5 PFLOP/s; HBM3E 8 TB/s.
-VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+# MI355X peaks.  VALU: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz = 78.64e12
+# full-rate 32-bit lane operations per second, i.e. the published fp32 vector
+# 157.3 TFLOP/s counted as FMAs.  bf16 dense MFMA 2.5 PFLOP/s.  HBM3E 8 TB/s.
+VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
 BF16_MFMA_FLOPS = 2.5e15
 HBM_BYTES_PER_S = 8.0e12
 
 # Algorithmic VALU issue slots per normal (one column of one token-draw) of
-# the fused gamma = 0 head kernel; each operation costs its issue slots on
-# gfx950 (full-rate = 1; transcendentals and 32x32->64 multiplies = 4, as
-# measured by the instruction-rate probe recorded in the design notes).
-#   Philox4x32-10, 1/4 block: 5 mulhilo32 (4 each) + 5 three-input xor (2 each)
-#   uniform map: 2;  Box-Muller, 1/2 pair: log, sqrt, sin, cos / 2 (4 each)
-#   + 1.5 multiplies;  perturb FMA 1 + exp2 4 + sum 1;  accumulate 2.
-SLOTS = {"philox": 5 * 4 + 5 * 2, "uniform": 2, "box_muller": 0.5 * 4 * 4 + 1.5,
-         "cross_entropy": 1 + 4 + 1, "accumulate": 2}
+# the fused gamma = 0 head kernel.  Issue cost on gfx950, measured with a
+# dependent-chain probe: 1 slot for fp32 add/mul/fma and 32-bit logic
+# (including v_bitop3), 2 for v_mad_u64_u32 and v_alignbit, 4 for the
+# transcendentals (v_exp, v_log, v_sqrt, v_sin, v_cos).
+#   Philox4x32-10 per block of 4 normals, counter (token, column/4, draw,
+#     stream): 16 lane-varying 32x32->64 products (2) + 18 xors (1) = 50 -> 12.5
+#   uniform map: alignbit + subtract = 3
+#   Box-Muller per pair: log, sqrt, cos, sin (4 each) + 3 multiplies = 19 -> 9.5
+#   perturbed cross-entropy: FMA + exp2 + add = 6
+#   accumulation of sum a and sum delta a: 2
+SLOTS = {"philox": (16 * 2 + 18) / 4, "uniform": 3, "box_muller": (4 * 4 + 3) / 2,
+         "cross_entropy": 6, "accumulate": 2}
 SLOTS_PER_NORMAL = sum(SLOTS.values())
+
+# Hardware byte counts of the head kernel (FETCH_SIZE and WRITE_SIZE from two
+# rocprofv3 --pmc runs, scaled by the same counters read on a plain copy of
+# known size) are kept in this summary with the hash of the kernel sources
+# they were taken on; they are reported only while the sources are unchanged.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "head_kernel_paper_traffic.json")
+KERNEL_SOURCES = ["activation_perturbation_estimator_amd/csrc/dust_head.hip",
+                  "activation_perturbation_estimator_amd/csrc/dust_device.hpp"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the kernel sources with comments and blank space removed, so
+    that editing a comment does not invalidate the recorded counters."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def parse():
@@ -53,6 +92,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain fp32 copy kernel (y = x * 1) over this "
+                         "many MiB: the reference that scales hardware byte counters")
     return ap.parse_args()
 
 
@@ -124,6 +166,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        xs = torch.ones(n, dtype=torch.float32, device=dev)
+        ys = torch.empty_like(xs)
+        torch.mul(xs, 1.0, out=ys)
+        torch.cuda.synchronize()
+        del xs, ys
+
     stage = [0.0] * (nev - 1)
     for row in evs:
         for s in range(nev - 1):
@@ -161,8 +211,8 @@ def main():
                    "seq_len": w.seq_len, "parallelism": "single GPU"},
         "roofline": {"bound": "alu", "kernel": "head_kernel (fused noise + CE + accumulate)"
                      if fused else "head_kernel (per-draw losses)",
-                     "achieved": achieved, "peak": peak, "unit": "Tslot/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
+                     "frac": achieved / peak, "traffic": measured_traffic(w.name),
                      "slots_per_normal": SLOTS_PER_NORMAL, "launch_ms": head_ms},
         "stages_ms": {"head": stage[0], "error_estimate": stage[1], "outer_sum": gemm_ms},
         "outer_sum": {"algorithmic_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12,

@@ -32,9 +32,9 @@
  *     N = layer output width (N = V for the LM head, N % 4 == 0), d = layer
  *     input width, K draws.
  *
- * Noise convention (the pages fix only "standard normal, independent per
- * token"; this library's counter-based stream, reproduced by
- * dust_noise):  a^(i)_t[n] for draw i, token t, column n comes from the
+ * Noise convention (the pages fix only that the noise is standard normal and
+ * independent per token; this is this library's counter-based stream, which
+ * dust_noise reproduces):  a^(i)_t[n] for draw i, token t, column n comes from the
  * Philox4x32-10 block (Salmon et al., SC'11) with key (seed mod 2^32,
  * seed >> 32) and counter words (t, n / 4, i, stream).  Each 32-bit output word
  * x becomes u = ((x >> 9) + 1/2) * 2^-23, and Box-Muller maps (u0,u1) to
@@ -166,7 +166,7 @@ dust_status dust_head_losses(const void* logits, dust_dtype logits_dt, const int
                              int64_t T, int64_t V, float sigma, int64_t K,
                              uint64_t seed, uint32_t stream, float* losses, dust_stream_t s);
 
-/* Centring (paper digest, section 2.2, "centred loss decrease"):
+/* Centring (paper digest, section 2.2: the centred loss decrease):
  * c[i,t] = mean_j x[j,t] - x[i,t] for per-draw losses x [K,T]; this is the
  * loss decrease d_i = l0 - l_i minus its mean over the draws, whatever the
  * clean loss l0.  x and c device [K,T] fp32; c may equal x (in place). */
