@@ -37,6 +37,7 @@ constexpr int kBN = 256;          // columns of G (layer inputs) per workgroup
 constexpr int kBT = 32;           // tokens per pipeline step
 constexpr int kRow = kBT + 8;     // bf16 per LDS row: 80 bytes, 16-byte aligned
 constexpr int kXcds = 8;          // MI355X: workgroups go round-robin to 8 XCDs
+constexpr int kGemmDepth = 1;     // steps of g / X^T loads in flight per thread (2 measured slower: 1 wave per SIMD)
 
 // Two fp32 values -> packed bf16 hi and packed bf16 lo (v_cvt_pk_bf16_f32, round
 // to nearest even): v = hi + lo + O(2^-17 |v|).
@@ -106,8 +107,9 @@ struct GemmGeom {
 // split; each wave owns 64 x 128 as 2 x 4 MFMA blocks.  Tokens advance 32 at a
 // time through two LDS stages: the next step's g and Xt are fetched into
 // registers while the matrix cores work on the current stage.
-template <bool kXF32>
-__global__ void __launch_bounds__(256, kXF32 ? 1 : 2)
+// kDepth: steps of global loads in flight (register sets).
+template <bool kXF32, int kDepth>
+__global__ void __launch_bounds__(256, kDepth > 1 || kXF32 ? 1 : 2)
 outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi,
                  const uint16_t* __restrict__ xt_lo, GemmGeom geo, float* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -156,16 +158,16 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi
   const int a_voff = (int)((m0 + arow) * 4);
   const int a_tstride = (int)(geo.M * 4);
 
-  float av[16];
-  uint4 bh[4], bl[kXF32 ? 4 : 1];
-  auto fetch = [&](int64_t t0) {
+  float av[kDepth][16];
+  uint4 bh[kDepth][4], bl[kDepth][kXF32 ? 4 : 1];
+  auto fetch = [&](int set, int64_t t0) {
     const int tl = (int)(t0 - t_begin);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tt = tl + 8 * (aq + 2 * qq) + e;
-        av[8 * qq + e] = __uint_as_float(
+        av[set][8 * qq + e] = __uint_as_float(
             __builtin_amdgcn_raw_buffer_load_b32(g_rsrc, a_voff + tt * a_tstride, 0, 0));
       }
 #pragma unroll
@@ -174,22 +176,22 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi
       const int off = (int)(((chunk >> 2) * geo.Tp + t0 + 8 * (chunk & 3)) * 2);
       typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
       u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xh_rsrc, off, 0, 0);
-      bh[k] = make_uint4(v.x, v.y, v.z, v.w);
+      bh[set][k] = make_uint4(v.x, v.y, v.z, v.w);
       if constexpr (kXF32) {
         u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(xl_rsrc, off, 0, 0);
-        bl[k] = make_uint4(w.x, w.y, w.z, w.w);
+        bl[set][k] = make_uint4(w.x, w.y, w.z, w.w);
       }
     }
   };
-  auto stash = [&](int stage) {
+  auto stash = [&](int set, int stage) {
     uint16_t* base = lds + stage * kStage;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       uint4 ph, pl;
-      split2(av[8 * qq + 0], av[8 * qq + 1], ph.x, pl.x);
-      split2(av[8 * qq + 2], av[8 * qq + 3], ph.y, pl.y);
-      split2(av[8 * qq + 4], av[8 * qq + 5], ph.z, pl.z);
-      split2(av[8 * qq + 6], av[8 * qq + 7], ph.w, pl.w);
+      split2(av[set][8 * qq + 0], av[set][8 * qq + 1], ph.x, pl.x);
+      split2(av[set][8 * qq + 2], av[set][8 * qq + 3], ph.y, pl.y);
+      split2(av[set][8 * qq + 4], av[set][8 * qq + 5], ph.z, pl.z);
+      split2(av[set][8 * qq + 6], av[set][8 * qq + 7], ph.w, pl.w);
       const int off = arow * kRow + 8 * (aq + 2 * qq);
       *reinterpret_cast<uint4*>(base + off) = ph;
       *reinterpret_cast<uint4*>(base + kA + off) = pl;
@@ -198,20 +200,13 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi
     for (int k = 0; k < 4; ++k) {
       const int chunk = tid + 256 * k;
       const int off = (chunk >> 2) * kRow + 8 * (chunk & 3);
-      *reinterpret_cast<uint4*>(base + 2 * kA + off) = bh[k];
-      if constexpr (kXF32) *reinterpret_cast<uint4*>(base + 2 * kA + kB + off) = bl[k];
+      *reinterpret_cast<uint4*>(base + 2 * kA + off) = bh[set][k];
+      if constexpr (kXF32) *reinterpret_cast<uint4*>(base + 2 * kA + kB + off) = bl[set][k];
     }
   };
 
-  if (nsteps > 0) {
-    fetch(t_begin);
-    stash(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const bool more = (s + 1 < nsteps);
-    if (more) fetch(t_begin + (int64_t)(s + 1) * kBT);
-    const uint16_t* base = lds + (s & 1) * kStage;
+  auto compute = [&](int stage) {
+    const uint16_t* base = lds + stage * kStage;
 #pragma unroll
     for (int kk = 0; kk < kBT; kk += 16) {
       const int koff = kk + 8 * (lane >> 5);
@@ -239,8 +234,26 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xt_hi
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fah[mb], fbl[nb], acc[mb][nb], 0, 0, 0);
         }
     }
-    if (more) stash((s + 1) & 1);
-    __syncthreads();
+  };
+
+  // Software pipeline: step s computes from LDS stage s%2 while register set
+  // (s+1)%kDepth is in flight from global memory and set s%kDepth, already
+  // stashed, is refilled with step s+kDepth.
+  for (int d = 0; d < kDepth; ++d)
+    if (d < nsteps) fetch(d, t_begin + (int64_t)d * kBT);
+  if (nsteps > 0) stash(0, 0);
+  __syncthreads();
+  for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int s = s0 + d;
+      if (s < nsteps) {
+        if (s + kDepth < nsteps) fetch(d, t_begin + (int64_t)(s + kDepth) * kBT);
+        compute(s & 1);
+        if (s + 1 < nsteps) stash((d + 1) % kDepth, (s + 1) & 1);
+        __syncthreads();
+      }
+    }
   }
 
   // Register r of block (mb, nb) holds row 8*(r/4) + 4*(lane/32) + r%4 and
@@ -331,13 +344,13 @@ static hipError_t launch_gemm_t(const GemmGeom& geo, const float* g, const uint1
   constexpr int kStageBytes = 2 * (2 * kBM * kRow + (kXF32 ? 2 : 1) * kBN * kRow);
   const size_t lds = 2 * (size_t)kStageBytes;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&outer_sum_kernel<kXF32>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&outer_sum_kernel<kXF32, kGemmDepth>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int64_t nwg = geo.groups_per_xcd * kXcds * geo.tiles_n;
-  hipLaunchKernelGGL(outer_sum_kernel<kXF32>, dim3((uint32_t)nwg), dim3(256), lds, s, g, xh, xl,
-                     geo, out);
+  hipLaunchKernelGGL((outer_sum_kernel<kXF32, kGemmDepth>), dim3((uint32_t)nwg), dim3(256), lds, s, g,
+                     xh, xl, geo, out);
   return hipGetLastError();
 }
 
