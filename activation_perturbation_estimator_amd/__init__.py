@@ -25,7 +25,9 @@ from ._lib import (DUST_BF16, DUST_F32, DUST_N_MAX, DUST_SIGMA_MAX, DUST_STAGE_E
 
 __all__ = [
     "head_estimate", "linear_estimate", "noise", "philox4x32_10", "head_losses", "centre",
-    "reward_scan", "error_estimate", "outer_sum", "check_targets", "head_workspace_size",
+    "reward_scan", "error_estimate", "outer_sum", "perturbed_linear", "embedding_grad",
+    "sgd_momentum_", "adam_", "ce_grad", "check_targets",
+    "head_workspace_size",
     "linear_workspace_size", "outer_sum_workspace_size", "version", "DustError",
     "DUST_SIGMA_MAX", "DUST_N_MAX", "DUST_STAGE_EVENTS",
 ]
@@ -240,6 +242,71 @@ def outer_sum(g_hat, X, out=None, workspace=None):
                             _stream(g_hat.device))
     _lib.check("dust_outer_sum", st)
     return G
+
+
+def perturbed_linear(X, W, *, sigma: float, seed: int = 1, stream: int = 0, draw0: int = 0,
+                     ndraw: int = 1, out=None):
+    """Y[k] = X W^T + sigma a^(draw0+k) as float32 [ndraw, T, N]: the caller's
+    perturbed forward, with the noise dust_linear_estimate regenerates."""
+    torch = _torch()
+    T, d = X.shape
+    N = W.shape[0]
+    if W.shape[1] != d or W.dtype != X.dtype:
+        raise ValueError("X [T,d] and W [N,d] must share d and dtype")
+    Y = torch.empty((ndraw, T, N), dtype=torch.float32, device=X.device) if out is None else out
+    st = _lib.load().dust_perturbed_linear(_dev(X, "X"), _dev(W, "W"), _dtype_code(X), T, d, N,
+                                           float(sigma), int(seed), int(stream), int(draw0),
+                                           int(ndraw), _dev(Y, "Y"), _stream(X.device))
+    _lib.check("dust_perturbed_linear", st)
+    return Y
+
+
+def embedding_grad(ids, g_hat, vocab: int, out=None, workspace=None):
+    """G_E[v] = sum_{t: ids[t] = v} g_hat[t] as float32 [vocab, N] (one-hot input:
+    the outer product is a scatter-add; deterministic order)."""
+    torch = _torch()
+    lib = _lib.load()
+    T, N = g_hat.shape
+    if ids.shape != (T,) or ids.dtype != torch.int32:
+        raise ValueError("ids must be int32 [T]")
+    G = torch.empty((vocab, N), dtype=torch.float32, device=g_hat.device) if out is None else out
+    ws = _workspace(lib.dust_embedding_workspace_size(T, vocab), g_hat.device, workspace)
+    st = lib.dust_embedding_grad(_dev(ids, "ids"), _dev(g_hat, "g_hat"), T, N, int(vocab),
+                                 _dev(G, "G_E"), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(g_hat.device))
+    _lib.check("dust_embedding_grad", st)
+    return G
+
+
+def sgd_momentum_(W, G, m, *, lr: float, momentum: float = 0.9, weight_decay: float = 0.0):
+    """In place: m = momentum m + (G + wd W); W -= lr m (float32 tensors of one size)."""
+    st = _lib.load().dust_sgd_momentum(_dev(W, "W"), _dev(G, "G"), _dev(m, "m"), W.numel(),
+                                       float(lr), float(momentum), float(weight_decay),
+                                       _stream(W.device))
+    _lib.check("dust_sgd_momentum", st)
+    return W
+
+
+def adam_(W, G, m, v, *, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+          eps: float = 1e-8, weight_decay: float = 0.0):
+    """In place Adam step (bias-corrected, PyTorch semantics) on float32 tensors."""
+    st = _lib.load().dust_adam(_dev(W, "W"), _dev(G, "G"), _dev(m, "m"), _dev(v, "v"), W.numel(),
+                               float(lr), float(beta1), float(beta2), float(eps),
+                               float(weight_decay), int(step), _stream(W.device))
+    _lib.check("dust_adam", st)
+    return W
+
+
+def ce_grad(logits, targets, out=None):
+    """softmax(z) - onehot(y) as float32 [T,V]: the closed-form LM-head gradient."""
+    torch = _torch()
+    T, V = logits.shape
+    o = torch.empty((T, V), dtype=torch.float32, device=logits.device) if out is None else out
+    st = _lib.load().dust_ce_grad(_dev(logits, "logits"), _dtype_code(logits),
+                                  _dev(targets, "targets"), T, V, _dev(o, "out"),
+                                  _stream(logits.device))
+    _lib.check("dust_ce_grad", st)
+    return o
 
 
 def check_targets(targets, V: int) -> bool:

@@ -260,6 +260,75 @@ dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, i
                                            aligned_base(workspace), as_stream(s)));
 }
 
+dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, int64_t T,
+                                  int64_t d, int64_t N, float sigma, uint64_t seed,
+                                  uint32_t stream, int64_t draw0, int64_t ndraw, float* Y,
+                                  dust_stream_t s) {
+  if (!X || !W || !Y || !dtype_ok(dt)) return DUST_ERR_INVALID_ARG;
+  if (T <= 0 || T > kMaxTokens || N <= 0 || N % 4 != 0 || d <= 0 || d % 8 != 0)
+    return DUST_ERR_INVALID_ARG;
+  if (N > ((int64_t)1 << 20) || d > ((int64_t)1 << 20)) return DUST_ERR_UNSUPPORTED;
+  if (!sigma_ok(sigma) || draw0 < 0 || ndraw < 0 || draw0 + ndraw > ((int64_t)1 << 32))
+    return DUST_ERR_INVALID_ARG;
+  if (ndraw * T > kMaxElems / N) return DUST_ERR_UNSUPPORTED;
+  // the operand windows of one 128-row tile stay inside 32-bit byte offsets
+  if (128 * d * (dt == DUST_F32 ? 4 : 2) > (((int64_t)1 << 31) - 1)) return DUST_ERR_UNSUPPORTED;
+  return hip_status(dust::launch_perturbed_linear(X, W, dt == DUST_BF16, T, N, d, sigma, seed,
+                                                  stream, (uint32_t)draw0, ndraw, Y,
+                                                  as_stream(s)));
+}
+
+size_t dust_embedding_workspace_size(int64_t T, int64_t vocab) {
+  if (T < 0 || vocab <= 0) return kAlign;
+  return dust::embedding_workspace_bytes(T, vocab) + kAlign;
+}
+
+dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,
+                                int64_t vocab, float* G_E, void* workspace,
+                                size_t workspace_bytes, dust_stream_t s) {
+  if (!ids || !g_hat || !G_E || T < 0 || N <= 0 || N % 4 != 0 || vocab <= 0)
+    return DUST_ERR_INVALID_ARG;
+  if (T > kMaxT || vocab > ((int64_t)1 << 24) || T * N > kMaxElems || vocab * N > kMaxElems)
+    return DUST_ERR_UNSUPPORTED;
+  if (((T + 1023) / 1024) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < dust_embedding_workspace_size(T, vocab))
+    return DUST_ERR_WORKSPACE;
+  return hip_status(dust::launch_embedding_grad(ids, g_hat, T, N, vocab, G_E,
+                                                aligned_base(workspace), as_stream(s)));
+}
+
+dust_status dust_sgd_momentum(float* W, const float* G, float* m, int64_t n, float lr,
+                              float momentum, float weight_decay, dust_stream_t s) {
+  if (n < 0 || (n > 0 && (!W || !G || !m))) return DUST_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(weight_decay))
+    return DUST_ERR_INVALID_ARG;
+  return hip_status(dust::launch_sgd_momentum(W, G, m, n, lr, momentum, weight_decay,
+                                              as_stream(s)));
+}
+
+dust_status dust_adam(float* W, const float* G, float* m, float* v, int64_t n, float lr,
+                      float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                      dust_stream_t s) {
+  if (n < 0 || (n > 0 && (!W || !G || !m || !v)) || step < 1) return DUST_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) ||
+      !(eps > 0.f) || !std::isfinite(eps) || !std::isfinite(weight_decay))
+    return DUST_ERR_INVALID_ARG;
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  if (!(bc1 > 0.0) || !(bc2 > 0.0)) return DUST_ERR_INVALID_ARG;
+  return hip_status(dust::launch_adam(W, G, m, v, n, lr, beta1, beta2, eps, weight_decay,
+                                      (float)(1.0 / bc1), (float)(1.0 / std::sqrt(bc2)),
+                                      as_stream(s)));
+}
+
+dust_status dust_ce_grad(const void* logits, dust_dtype dt, const int32_t* targets, int64_t T,
+                         int64_t V, float* out, dust_stream_t s) {
+  if (!logits || !targets || !out || !dtype_ok(dt) || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxTokens || T * V > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  return hip_status(dust::launch_ce_grad(logits, dt == DUST_BF16, targets, T, V, out,
+                                         as_stream(s)));
+}
+
 dust_status dust_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
                                dust_stream_t s_) {
   if (!targets || !flag || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;

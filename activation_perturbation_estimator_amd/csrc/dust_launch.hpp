@@ -45,6 +45,25 @@ size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d);
 hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
                             int64_t d, float* G, void* workspace, hipStream_t s);
 
+// Perturbed forward of a linear layer: Y[k] = X W^T + sigma a^(draw0+k).
+hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int64_t T, int64_t N,
+                                   int64_t d, float sigma, uint64_t seed, uint32_t stream,
+                                   uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s);
+
+// Embedding rows: G_E[v] = sum_{t: ids[t] = v} g_t, deterministic order.
+size_t embedding_workspace_bytes(int64_t T, int64_t vocab);
+hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, int64_t N,
+                                 int64_t vocab, float* GE, void* workspace, hipStream_t s);
+
+// Optimiser steps and the closed-form head gradient.
+hipError_t launch_sgd_momentum(float* W, const float* G, float* M, int64_t n, float lr, float mu,
+                               float wd, hipStream_t s);
+hipError_t launch_adam(float* W, const float* G, float* M, float* V, int64_t n, float lr, float b1,
+                       float b2, float eps, float wd, float inv_bc1, float inv_sqrt_bc2,
+                       hipStream_t s);
+hipError_t launch_ce_grad(const void* logits, bool bf16, const int32_t* targets, int64_t T,
+                          int64_t V, float* out, hipStream_t s);
+
 // Target range check; flag must be a device int32.
 hipError_t launch_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
                                 hipStream_t s);

@@ -88,7 +88,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="paper",
-                    help="paper (default: T=16384, V=4096, d=512, K=64), k1024, k16384, tiny")
+                    help="paper (default: T=16384, V=4096, d=512, K=64), k1024, k16384, tiny, "
+                         "linear (hidden layer 512->2048, K=256, gamma=0.9)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -124,6 +125,158 @@ def cpu_baseline(w, z, y, target_s: float):
                       f"(g_hat rows, fp64, OpenMP over tokens), {dt:.2f} s"}
 
 
+def time_steps(torch, step, steps: int, warmup: int, nev: int, copy_probe_mib: int = 0):
+    """Warm-up, then `steps` timed calls bracketed by device synchronisation;
+    returns (ms per step, per-stage ms per launch) from the library's stage events."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    for row in evs:  # materialise the handles on this stream before timing
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if copy_probe_mib:
+        n = copy_probe_mib * (1 << 20) // 4
+        xs = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        ys = torch.empty_like(xs)
+        torch.mul(xs, 1.0, out=ys)
+        torch.cuda.synchronize()
+        del xs, ys
+    stage = [0.0] * (nev - 1)
+    for row in evs:
+        for s in range(nev - 1):
+            stage[s] += row[s].elapsed_time(row[s + 1])
+    return wall * 1e3 / steps, [v / steps for v in stage]
+
+
+def common_fields(args, w, value, ms_per_step, metric, workload_text):
+    return {
+        "metric": metric, "value": value, "unit": "token-draws/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload_text, "T": w.T, "N": w.V, "d": w.d, "K": w.K,
+                   "global_batch": w.T, "seq_len": w.seq_len, "parallelism": "single GPU"},
+    }
+
+
+def outer_sum_fields(w, gemm_ms):
+    flops = 2.0 * w.T * w.V * w.d
+    return {"algorithmic_tflops": flops / (gemm_ms / 1e3) / 1e12,
+            "executed_bf16_tflops": 2 * flops / (gemm_ms / 1e3) / 1e12,
+            "peak_bf16_tflops": BF16_MFMA_FLOPS / 1e12}
+
+
+def run_head(args, torch, dust, synth, w):
+    z, y, X = synth.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    zd, yd, Xd = z.to(dev), y.to(dev), X.to(dev)
+    g = torch.empty((w.T, w.V), dtype=torch.float32, device=dev)
+    G = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(dust.head_workspace_size(w.T, w.V, w.d, w.K, w.gamma), dtype=torch.uint8,
+                     device=dev)
+
+    def step(events):
+        dust.head_estimate(zd, yd, Xd, sigma=w.sigma, K=w.K, gamma=w.gamma, seed=w.philox_seed,
+                           seq_len=w.seq_len, workspace=ws, out=(g, G), stage_events=events)
+
+    ms_per_step, stage = time_steps(torch, step, args.steps, args.warmup,
+                                    dust.DUST_STAGE_EVENTS, args.copy_probe_mib)
+    value = w.T * w.K / (ms_per_step / 1e3)
+    fused = (w.gamma == 0.0)
+    head_ms = stage[0]
+    achieved = float(w.T) * w.K * w.V * SLOTS_PER_NORMAL / (head_ms / 1e3) / 1e12
+    peak = VALU_SLOTS_PER_S / 1e12
+    out = common_fields(args, w, value, ms_per_step, METRIC,
+                        f"{w.name}: LM head T={w.T} ({w.T // w.seq_len}x{w.seq_len}), V={w.V}, "
+                        f"d={w.d}, K={w.K}, sigma={w.sigma}, gamma={w.gamma}, "
+                        f"{'bf16' if w.bf16 else 'fp32'} logits and X")
+    out["roofline"] = {"bound": "alu", "kernel": "head_kernel (fused noise + CE + accumulate)"
+                       if fused else "head_kernel (per-draw losses)",
+                       "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
+                       "frac": achieved / peak, "traffic": measured_traffic(w.name),
+                       "slots_per_normal": SLOTS_PER_NORMAL, "launch_ms": head_ms}
+    out["stages_ms"] = {"head": stage[0], "error_estimate": stage[1], "outer_sum": stage[2]}
+    out["outer_sum"] = outer_sum_fields(w, stage[2])
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, z, y, args.cpu_seconds)
+    return out
+
+
+# Error-estimate kernel, per normal: the noise (Philox 12.5 + uniform map 3 +
+# Box-Muller 9.5 slots) and one FMA.
+SLOTS_PER_NORMAL_ERROR_ESTIMATE = SLOTS["philox"] + SLOTS["uniform"] + SLOTS["box_muller"] + 1
+
+
+def cpu_baseline_linear(w, c, target_s: float):
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.num_threads()
+    cd = c.double().numpy()
+    rng = np.random.default_rng(1)
+    n = max(cores, 8)
+    while True:
+        tok = np.sort(rng.choice(w.T, size=min(n, w.T), replace=False))
+        t0 = time.perf_counter()
+        oracle.linear_rows(cd, w.seq_len, w.V, w.sigma, w.gamma, w.philox_seed, tok)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= w.T or dt * 2 * (target_s / max(dt, 1e-3)) > 6 * target_s:
+            break
+        n = min(w.T, int(n * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
+    return {"value": len(tok) * w.K / dt, "unit": "token-draws/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(tok)} of {w.T} tokens x all {w.K} draws of the same workload "
+                      f"(reward scan over all tokens, g_hat rows, fp64), {dt:.2f} s"}
+
+
+def run_linear(args, torch, dust, synth, w):
+    X, c = synth.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    Xd, cd = X.to(dev), c.to(dev)
+    g = torch.empty((w.T, w.V), dtype=torch.float32, device=dev)
+    G = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(dust.linear_workspace_size(w.T, w.d, w.V, w.K, w.gamma), dtype=torch.uint8,
+                     device=dev)
+
+    def step(events):
+        dust.linear_estimate(Xd, cd, N=w.V, sigma=w.sigma, gamma=w.gamma, seed=w.philox_seed,
+                             seq_len=w.seq_len, workspace=ws, out=(g, G), stage_events=events)
+
+    ms_per_step, stage = time_steps(torch, step, args.steps, args.warmup,
+                                    dust.DUST_STAGE_EVENTS, args.copy_probe_mib)
+    value = w.T * w.K / (ms_per_step / 1e3)
+    ee_ms = stage[1]
+    achieved = (float(w.T) * w.K * w.V * SLOTS_PER_NORMAL_ERROR_ESTIMATE / (ee_ms / 1e3) / 1e12)
+    peak = VALU_SLOTS_PER_S / 1e12
+    scan_bytes = 8.0 * w.T * w.K  # read c, write r
+    out = common_fields(args, w, value, ms_per_step,
+                        "token-draws/sec, hidden linear layer Dust estimator "
+                        f"(T={w.T}, N={w.V}, d_in={w.d})",
+                        f"{w.name}: linear d_in={w.d} -> N={w.V}, T={w.T} "
+                        f"({w.T // w.seq_len}x{w.seq_len}), K={w.K}, sigma={w.sigma}, "
+                        f"gamma={w.gamma}, bf16 X, caller c fp32")
+    out["roofline"] = {"bound": "alu", "kernel": "error_estimate_kernel (noise + r a accumulate)",
+                       "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
+                       "frac": achieved / peak, "traffic": None,
+                       "slots_per_normal": SLOTS_PER_NORMAL_ERROR_ESTIMATE, "launch_ms": ee_ms}
+    out["reward_scan"] = {"bound": "hbm", "achieved": scan_bytes / (stage[0] / 1e3) / 1e9,
+                          "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+                          "frac": scan_bytes / (stage[0] / 1e3) / HBM_BYTES_PER_S,
+                          "launch_ms": stage[0]}
+    out["stages_ms"] = {"reward_scan": stage[0], "error_estimate": stage[1], "outer_sum": stage[2]}
+    out["outer_sum"] = outer_sum_fields(w, stage[2])
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_linear(w, c, args.cpu_seconds)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,92 +289,8 @@ def main():
     from activation_perturbation_estimator_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.kind != "head":
-        sys.exit("bench.py times the LM-head estimator; pick a head workload")
-    z, y, X = synth.workload_inputs(w)
-    dev = torch.device("cuda:0")
-    zd, yd, Xd = z.to(dev), y.to(dev), X.to(dev)
-    g = torch.empty((w.T, w.V), dtype=torch.float32, device=dev)
-    G = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(dust.head_workspace_size(w.T, w.V, w.d, w.K, w.gamma), dtype=torch.uint8,
-                     device=dev)
-    nev = dust.DUST_STAGE_EVENTS
-
-    def step(events=None):
-        dust.head_estimate(zd, yd, Xd, sigma=w.sigma, K=w.K, gamma=w.gamma, seed=w.philox_seed,
-                           seq_len=w.seq_len, workspace=ws, out=(g, G), stage_events=events)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    for row in evs:  # materialise the handles on this stream before timing
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        xs = torch.ones(n, dtype=torch.float32, device=dev)
-        ys = torch.empty_like(xs)
-        torch.mul(xs, 1.0, out=ys)
-        torch.cuda.synchronize()
-        del xs, ys
-
-    stage = [0.0] * (nev - 1)
-    for row in evs:
-        for s in range(nev - 1):
-            stage[s] += row[s].elapsed_time(row[s + 1])
-    stage = [v / args.steps for v in stage]  # ms per launch of each stage
-    ms_per_step = wall * 1e3 / args.steps
-    token_draws = w.T * w.K
-    value = token_draws / (ms_per_step / 1e3)
-
-    fused = (w.gamma == 0.0)
-    head_ms = stage[0]
-    normals = float(w.T) * w.K * w.V
-    slots = normals * SLOTS_PER_NORMAL
-    achieved = slots / (head_ms / 1e3) / 1e12
-    peak = VALU_SLOTS_PER_S / 1e12
-    gemm_ms = stage[2]
-    gemm_flops = 2.0 * w.T * w.V * w.d
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "token-draws/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"{w.name}: LM head T={w.T} ({w.T // w.seq_len}x{w.seq_len}), "
-                               f"V={w.V}, d={w.d}, K={w.K}, sigma={w.sigma}, gamma={w.gamma}, "
-                               f"{'bf16' if w.bf16 else 'fp32'} logits and X",
-                   "T": w.T, "V": w.V, "d": w.d, "K": w.K, "global_batch": w.T,
-                   "seq_len": w.seq_len, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "kernel": "head_kernel (fused noise + CE + accumulate)"
-                     if fused else "head_kernel (per-draw losses)",
-                     "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(w.name),
-                     "slots_per_normal": SLOTS_PER_NORMAL, "launch_ms": head_ms},
-        "stages_ms": {"head": stage[0], "error_estimate": stage[1], "outer_sum": gemm_ms},
-        "outer_sum": {"algorithmic_tflops": gemm_flops / (gemm_ms / 1e3) / 1e12,
-                      "executed_bf16_tflops": 2 * gemm_flops / (gemm_ms / 1e3) / 1e12,
-                      "peak_bf16_tflops": BF16_MFMA_FLOPS / 1e12},
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, z, y, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    run = run_linear if w.kind == "linear" else run_head
+    print(json.dumps(run(args, torch, dust, synth, w)), flush=True)
 
 
 if __name__ == "__main__":

@@ -195,6 +195,50 @@ dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt,
 
 size_t dust_outer_sum_workspace_size(int64_t T, int64_t N, int64_t d);
 
+/* Perturbed forward of a hidden linear layer y = W x (paper digest, sections 2
+ * and 2.1; laoyaoba analysis, mechanism section): for k < ndraw,
+ *   Y[k,t,n] = sum_j X[t,j] W[n,j] + sigma a^(draw0+k)_t[n],
+ * the noise from the same (seed, stream) counters that dust_linear_estimate
+ * regenerates, so a caller's perturbed forwards and its estimate agree.
+ *   X device [T,d] and W device [N,d] (PyTorch Linear layout), both of dtype dt
+ *   (bf16 operands multiply exactly; fp32 operands are split into bf16 hi + lo)
+ *   Y device [ndraw,T,N] fp32 out
+ * Requires N % 4 == 0, d % 8 == 0, 0 < sigma <= DUST_SIGMA_MAX (sigma = 0 is
+ * rejected: use a plain GEMM), T <= 2^31, N, d <= 2^20. */
+dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, int64_t T,
+                                  int64_t d, int64_t N, float sigma, uint64_t seed,
+                                  uint32_t stream, int64_t draw0, int64_t ndraw, float* Y,
+                                  dust_stream_t s);
+
+/* Embedding layer (paper digest, section 2.2: a one-hot input turns the outer
+ * product into a scatter-add): G_E[v,:] = sum over tokens t with ids[t] = v of
+ * g_hat[t,:], summed in increasing t (deterministic; rows of unused ids are 0;
+ * ids outside [0, vocab) are skipped).
+ *   ids device [T] int32; g_hat device [T,N] fp32 (N % 4 == 0);
+ *   G_E device [vocab,N] fp32 out; workspace >= dust_embedding_workspace_size. */
+dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,
+                                int64_t vocab, float* G_E, void* workspace,
+                                size_t workspace_bytes, dust_stream_t s);
+size_t dust_embedding_workspace_size(int64_t T, int64_t vocab);
+
+/* Optimiser steps on a weight gradient (linlog explainer, experiment setup:
+ * SGD with momentum; paper digest, section 3.3: Adam).  All arrays device fp32
+ * [n], updated in place; G_W approximates +dL/dW, so W moves against it.
+ *   SGD:  m = momentum m + (G + wd W);  W -= lr m   (PyTorch SGD, dampening 0)
+ *   Adam: g = G + wd W; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ *         W -= lr/(1-b1^step) m / (sqrt(v)/sqrt(1-b2^step) + eps)  (step >= 1) */
+dust_status dust_sgd_momentum(float* W, const float* G, float* m, int64_t n, float lr,
+                              float momentum, float weight_decay, dust_stream_t s);
+dust_status dust_adam(float* W, const float* G, float* m, float* v, int64_t n, float lr,
+                      float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                      dust_stream_t s);
+
+/* Closed-form LM-head gradient dCE/dz = softmax(z_t) - onehot(y_t) (paper
+ * digest, section 4.2: the backprop gradient the estimate is compared with).
+ *   logits device [T,V] (dtype dt), targets device [T] int32, out device [T,V] fp32. */
+dust_status dust_ce_grad(const void* logits, dust_dtype dt, const int32_t* targets, int64_t T,
+                         int64_t V, float* out, dust_stream_t s);
+
 /* Checks 0 <= targets[t] < V for all t; waits on s for the answer.
  * Returns DUST_OK or DUST_ERR_TARGETS.  `flag` is a device int32 the call
  * overwrites (caller-owned scratch). */

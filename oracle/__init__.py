@@ -80,6 +80,18 @@ def _load():
     lib.oracle_linear_rows.argtypes = [_f64p, _i64, _i64, _i64, _f64, _i64, _f64, _u64,
                                        _u32, _i64p, _i64, _f64p]
     lib.oracle_linear_rows.restype = ctypes.c_int
+    lib.oracle_perturbed_linear.argtypes = [_f64p, _f64p, _i64, _i64, _i64, _f64, _u64, _u32,
+                                            _i64, _i64, _f64p]
+    lib.oracle_perturbed_linear.restype = ctypes.c_int
+    lib.oracle_embedding_grad.argtypes = [_i32p, _f64p, _i64, _i64, _i64, _f64p]
+    lib.oracle_embedding_grad.restype = ctypes.c_int
+    lib.oracle_sgd_momentum.argtypes = [_f64p, _f64p, _f64p, _i64, _f64, _f64, _f64]
+    lib.oracle_sgd_momentum.restype = None
+    lib.oracle_adam.argtypes = [_f64p, _f64p, _f64p, _f64p, _i64, _f64, _f64, _f64, _f64, _f64,
+                                _i64]
+    lib.oracle_adam.restype = None
+    lib.oracle_ce_grad.argtypes = [_f64p, _i32p, _i64, _i64, _f64p]
+    lib.oracle_ce_grad.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -230,3 +242,60 @@ def linear_rows(c, seq_len: int, N: int, sigma: float, gamma: float, seed: int, 
     if rc != 0:
         raise ValueError("oracle_linear_rows rejected its arguments")
     return rows
+
+
+def perturbed_linear(X, W, sigma: float, seed: int, stream: int = 0, draw0: int = 0,
+                     ndraw: int = 1) -> np.ndarray:
+    """Y[k] = X W^T + sigma a^(draw0+k): the perturbed forward of a hidden linear
+    layer (paper digest, sections 2 and 2.1)."""
+    Xd = _f64c(X)
+    Wd = _f64c(W)
+    T, d = Xd.shape
+    N = Wd.shape[0]
+    Y = np.empty((ndraw, T, N), dtype=np.float64)
+    rc = _load().oracle_perturbed_linear(Xd, Wd, T, d, N, float(sigma), int(seed), int(stream),
+                                         int(draw0), int(ndraw), Y)
+    if rc != 0:
+        raise ValueError("oracle_perturbed_linear rejected its arguments")
+    return Y
+
+
+def embedding_grad(ids, g, vocab: int) -> np.ndarray:
+    """G_E[v] = sum_{t: ids[t]=v} g[t] (paper digest, section 2.2: one-hot input)."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    gd = _f64c(g)
+    T, N = gd.shape
+    GE = np.empty((vocab, N), dtype=np.float64)
+    if _load().oracle_embedding_grad(ids, gd, T, N, int(vocab), GE) != 0:
+        raise ValueError("oracle_embedding_grad rejected its arguments")
+    return GE
+
+
+def sgd_momentum(W, G, m, lr: float, momentum: float, weight_decay: float = 0.0):
+    """One SGD-with-momentum step; returns (W, m) as new fp64 arrays."""
+    W = _f64c(W).copy()
+    m = _f64c(m).copy()
+    _load().oracle_sgd_momentum(W.ravel(), _f64c(G).ravel(), m.ravel(), W.size, float(lr),
+                                float(momentum), float(weight_decay))
+    return W, m
+
+
+def adam(W, G, m, v, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+         eps: float = 1e-8, weight_decay: float = 0.0):
+    """One bias-corrected Adam step; returns (W, m, v) as new fp64 arrays."""
+    W = _f64c(W).copy()
+    m = _f64c(m).copy()
+    v = _f64c(v).copy()
+    _load().oracle_adam(W.ravel(), _f64c(G).ravel(), m.ravel(), v.ravel(), W.size, float(lr),
+                        float(beta1), float(beta2), float(eps), float(weight_decay), int(step))
+    return W, m, v
+
+
+def ce_grad(logits, targets) -> np.ndarray:
+    """softmax(z_t) - onehot(y_t) in fp64."""
+    z = _f64c(logits)
+    y = np.ascontiguousarray(np.asarray(targets, dtype=np.int32))
+    T, V = z.shape
+    out = np.empty((T, V), dtype=np.float64)
+    _load().oracle_ce_grad(z, y, T, V, out)
+    return out

@@ -392,6 +392,89 @@ int oracle_linear_rows(const double* c, int64_t T, int64_t N, int64_t L,
     return 0;
 }
 
+/* ------------------------------------------------------------------------- */
+/* Perturbed forward of a hidden linear layer ([P2] sections 2 and 2.1: the   */
+/* layer's output y_t = W x_t is jittered to y_t + sigma a_t per token):      */
+/*   Y[k][t][n] = sum_j X[t][j] W[n][j] + sigma a^(draw0+k)_t[n].              */
+/* X [T,d], W [N,d]; Y [ndraw,T,N].                                           */
+/* ------------------------------------------------------------------------- */
+int oracle_perturbed_linear(const double* X, const double* W, int64_t T, int64_t d, int64_t N,
+                            double sigma, uint64_t seed, uint32_t stream, int64_t draw0,
+                            int64_t ndraw, double* Y)
+{
+    if (T <= 0 || d <= 0 || N <= 0 || N % 4 != 0 || ndraw < 0) return -1;
+    #pragma omp parallel
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)N);
+        #pragma omp for schedule(static)
+        for (int64_t kt = 0; kt < ndraw * T; ++kt) {
+            int64_t k = kt / T, t = kt % T;
+            noise_row(seed, stream, draw0 + k, t, N, a);
+            for (int64_t n = 0; n < N; ++n) {
+                double y = 0.0;
+                for (int64_t j = 0; j < d; ++j) y += X[t * d + j] * W[n * d + j];
+                Y[(k * T + t) * N + n] = y + sigma * a[n];
+            }
+        }
+        free(a);
+    }
+    return 0;
+}
+
+/* Embedding layer ([P2] section 2.2: one-hot input, so the outer product is a
+ * scatter-add): G_E[v] = sum_{t: ids[t] = v} g[t]; ids outside [0, vocab)
+ * contribute nothing. */
+int oracle_embedding_grad(const int32_t* ids, const double* g, int64_t T, int64_t N,
+                          int64_t vocab, double* GE)
+{
+    if (T < 0 || N <= 0 || vocab <= 0) return -1;
+    for (int64_t e = 0; e < vocab * N; ++e) GE[e] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t v = ids[t];
+        if (v < 0 || v >= vocab) continue;
+        for (int64_t n = 0; n < N; ++n) GE[v * N + n] += g[t * N + n];
+    }
+    return 0;
+}
+
+/* SGD with momentum (linlog explainer, setup): m = mu m + (G + wd W); W -= lr m. */
+void oracle_sgd_momentum(double* W, const double* G, double* m, int64_t n, double lr, double mu,
+                         double wd)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double g = G[i] + wd * W[i];
+        m[i] = mu * m[i] + g;
+        W[i] -= lr * m[i];
+    }
+}
+
+/* Adam (paper digest, section 3.3), bias-corrected at step k >= 1. */
+void oracle_adam(double* W, const double* G, double* m, double* v, int64_t n, double lr,
+                 double b1, double b2, double eps, double wd, int64_t k)
+{
+    double bc1 = 1.0 - pow(b1, (double)k), bc2 = 1.0 - pow(b2, (double)k);
+    for (int64_t i = 0; i < n; ++i) {
+        double g = G[i] + wd * W[i];
+        m[i] = b1 * m[i] + (1.0 - b1) * g;
+        v[i] = b2 * v[i] + (1.0 - b2) * g * g;
+        W[i] -= (lr / bc1) * m[i] / (sqrt(v[i]) / sqrt(bc2) + eps);
+    }
+}
+
+/* Closed-form LM-head gradient: softmax(z_t) - onehot(y_t). */
+void oracle_ce_grad(const double* z, const int32_t* y, int64_t T, int64_t V, double* out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const double* zr = z + t * V;
+        double m = zr[0];
+        for (int64_t v = 1; v < V; ++v) if (zr[v] > m) m = zr[v];
+        double s = 0.0;
+        for (int64_t v = 0; v < V; ++v) s += exp(zr[v] - m);
+        for (int64_t v = 0; v < V; ++v)
+            out[t * V + v] = exp(zr[v] - m) / s - (v == y[t] ? 1.0 : 0.0);
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -1,0 +1,92 @@
+"""GPU consumers of the estimate against the oracle: the embedding scatter-add
+(bit-exact run to run), the optimiser steps, the closed-form head gradient,
+and the cosine-versus-population harness, whose fitted law must show c near
+V + 1 (first-order analysis of the estimator; the pages fit the same form,
+paper digest, section 4.2)."""
+import numpy as np
+import pytest
+
+import oracle
+from activation_perturbation_estimator_amd import synth
+from util import need_gpu, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T,N,vocab", [(3000, 100, 257), (1, 4, 3), (2048, 8, 1),
+                                       (16384, 4096, 4096)])
+def test_embedding_grad(T, N, vocab):
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(T + N)
+    ids = synth.zipf_targets(rng, T, vocab)
+    if T > 10:
+        ids[::97] = -3          # out-of-range ids are skipped
+        ids[5::101] = vocab
+    g = rng.standard_normal((T, N)).astype(np.float32)
+    gi, gg = torch.from_numpy(ids).cuda(), torch.from_numpy(g).cuda()
+    a = dust.embedding_grad(gi, gg, vocab)
+    b = dust.embedding_grad(gi, gg, vocab)
+    torch.cuda.synchronize()
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert np.array_equal(a, b)
+    ref = oracle.embedding_grad(ids, g.astype(np.float64), vocab)
+    assert rel_l2(a, ref) <= 1e-6, rel_l2(a, ref)
+    used = np.zeros(vocab, bool)
+    used[ids[(ids >= 0) & (ids < vocab)]] = True
+    assert np.all(a[~used] == 0)
+
+
+def test_sgd_and_adam_steps():
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(4)
+    n = 1_000_003
+    W0 = rng.standard_normal(n).astype(np.float32)
+    Gs = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+    W = torch.from_numpy(W0.copy()).cuda()
+    m = torch.zeros(n, device="cuda")
+    Wr, mr = W0.astype(np.float64), np.zeros(n)
+    for G in Gs:
+        dust.sgd_momentum_(W, torch.from_numpy(G).cuda(), m, lr=0.05, momentum=0.9,
+                           weight_decay=0.01)
+        Wr, mr = oracle.sgd_momentum(Wr, G, mr, 0.05, 0.9, 0.01)
+    torch.cuda.synchronize()
+    assert rel_l2(W.cpu().numpy(), Wr) <= 1e-6
+    W = torch.from_numpy(W0.copy()).cuda()
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    Wr, mr, vr = W0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for k, G in enumerate(Gs, start=1):
+        dust.adam_(W, torch.from_numpy(G).cuda(), m, v, lr=0.01, step=k, beta1=0.9, beta2=0.99,
+                   eps=1e-6, weight_decay=0.02)
+        Wr, mr, vr = oracle.adam(Wr, G, mr, vr, 0.01, k, 0.9, 0.99, 1e-6, 0.02)
+    torch.cuda.synchronize()
+    assert np.abs(W.cpu().numpy() - Wr).max() <= 1e-5
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_ce_grad(bf16):
+    dust = need_gpu()
+    import torch
+    z, y, _ = synth.head_inputs(300, 1000, 4, seed=5, bf16=bf16, logit_var=4.0)
+    got = dust.ce_grad(z.cuda(), y.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.ce_grad(synth.to_f64(z), y.numpy())
+    assert np.abs(got.cpu().numpy() - ref).max() <= 2e-6
+
+
+def test_cosine_harness_recovers_the_law():
+    dust = need_gpu()
+    import torch
+    from activation_perturbation_estimator_amd.cosine import cosine_sweep
+    T, V = 64, 512
+    z, y, X = synth.head_inputs(T, V, 32, seed=6)
+    res = cosine_sweep(z.cuda(), y.cuda(), X.cuda(), [16, 64, 256, 1024, 4096, 16384],
+                       sigma=0.005, seed=3)
+    cos = res["cos_token_mean"]
+    assert all(a < b for a, b in zip(cos, cos[1:]))
+    fit = res["fit_token"]
+    assert 0.8 * (V + 1) <= fit["c"] <= 1.2 * (V + 1), fit
+    assert fit["c_max"] >= 0.99 and fit["rmse"] < 0.02, fit
+    assert res["cos_GW"][-1] > res["cos_GW"][0]

@@ -104,3 +104,16 @@ def test_linear_rows_agree_with_full_estimate():
     np.testing.assert_allclose(oracle.linear_rows(c, L, N, 0.2, 0.9, 5, tok), g[tok],
                                rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(G, oracle.outer_sum(g, X), rtol=1e-12)
+
+
+def test_perturbed_linear_is_product_plus_noise():
+    # Y[k] = X W^T + sigma a^(draw0+k): against numpy's matmul and the (pinned)
+    # noise stream; linear in sigma.
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((9, 16))
+    W = rng.standard_normal((12, 16))
+    Y = oracle.perturbed_linear(X, W, 0.3, seed=4, stream=2, draw0=5, ndraw=3)
+    a = oracle.noise(4, 2, 5, 3, 9, 12)
+    np.testing.assert_allclose(Y, (X @ W.T)[None] + 0.3 * a, rtol=1e-12, atol=1e-12)
+    Y2 = oracle.perturbed_linear(X, W, 0.6, seed=4, stream=2, draw0=5, ndraw=3)
+    np.testing.assert_allclose(Y2 - Y, 0.3 * a, rtol=1e-12, atol=1e-12)
