@@ -25,7 +25,8 @@ def fit_law(Ks, cos) -> Dict[str, float]:
     Ks = np.asarray(Ks, dtype=np.float64)
     cos = np.asarray(cos, dtype=np.float64)
     (cmax, c), _ = curve_fit(lambda k, cm, cc: cm / np.sqrt(1.0 + cc / k), Ks, cos,
-                             p0=(1.0, float(Ks.max()) / 8), maxfev=20000)
+                             p0=(1.0, float(Ks.max()) / 8),
+                             bounds=([0.0, 0.0], [2.0, np.inf]), maxfev=20000)
     resid = cos - cmax / np.sqrt(1.0 + c / Ks)
     return {"c_max": float(cmax), "c": float(c), "rmse": float(np.sqrt(np.mean(resid ** 2)))}
 
