@@ -270,7 +270,7 @@ def embedding_grad(ids, g_hat, vocab: int, out=None, workspace=None):
     if ids.shape != (T,) or ids.dtype != torch.int32:
         raise ValueError("ids must be int32 [T]")
     G = torch.empty((vocab, N), dtype=torch.float32, device=g_hat.device) if out is None else out
-    ws = _workspace(lib.dust_embedding_workspace_size(T, vocab), g_hat.device, workspace)
+    ws = _workspace(lib.dust_embedding_workspace_size(T, N, int(vocab)), g_hat.device, workspace)
     st = lib.dust_embedding_grad(_dev(ids, "ids"), _dev(g_hat, "g_hat"), T, N, int(vocab),
                                  _dev(G, "G_E"), ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream(g_hat.device))

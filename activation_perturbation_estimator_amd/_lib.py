@@ -54,7 +54,7 @@ SIGNATURES = {
     "dust_perturbed_linear": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _u64, _u32, _i64,
                                      _i64, _vp, _vp]),
     "dust_embedding_grad": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
-    "dust_embedding_workspace_size": (_sz, [_i64, _i64]),
+    "dust_embedding_workspace_size": (_sz, [_i64, _i64, _i64]),
     "dust_sgd_momentum": (_int, [_vp, _vp, _vp, _i64, _f32, _f32, _f32, _vp]),
     "dust_adam": (_int, [_vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "dust_ce_grad": (_int, [_vp, _int, _vp, _i64, _i64, _vp, _vp]),

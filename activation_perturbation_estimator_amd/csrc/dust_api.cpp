@@ -278,9 +278,9 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
                                                   as_stream(s)));
 }
 
-size_t dust_embedding_workspace_size(int64_t T, int64_t vocab) {
-  if (T < 0 || vocab <= 0) return kAlign;
-  return dust::embedding_workspace_bytes(T, vocab) + kAlign;
+size_t dust_embedding_workspace_size(int64_t T, int64_t N, int64_t vocab) {
+  if (T < 0 || N <= 0 || vocab <= 0) return kAlign;
+  return dust::embedding_workspace_bytes(T, N, vocab) + kAlign;
 }
 
 dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,
@@ -290,8 +290,8 @@ dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t 
     return DUST_ERR_INVALID_ARG;
   if (T > kMaxT || vocab > ((int64_t)1 << 24) || T * N > kMaxElems || vocab * N > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
-  if (((T + 1023) / 1024) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < dust_embedding_workspace_size(T, vocab))
+  if (((T + 511) / 512) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < dust_embedding_workspace_size(T, N, vocab))
     return DUST_ERR_WORKSPACE;
   return hip_status(dust::launch_embedding_grad(ids, g_hat, T, N, vocab, G_E,
                                                 aligned_base(workspace), as_stream(s)));

@@ -51,7 +51,7 @@ hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int6
                                    uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s);
 
 // Embedding rows: G_E[v] = sum_{t: ids[t] = v} g_t, deterministic order.
-size_t embedding_workspace_bytes(int64_t T, int64_t vocab);
+size_t embedding_workspace_bytes(int64_t T, int64_t N, int64_t vocab);
 hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, int64_t N,
                                  int64_t vocab, float* GE, void* workspace, hipStream_t s);
 

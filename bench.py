@@ -11,6 +11,10 @@ bounded sample of the same workload.
 
   python bench.py [--steps 10] [--warmup 2] [--workload paper] [--no-cpu-baseline]
                   [--copy-probe-mib 256]
+
+Other workloads print their own line: linear (the hidden-layer estimator),
+forward (perturbed forward), embedding, optim (SGD/Adam steps), cosine (the
+cosine-versus-population sweep and its fitted law).
 """
 from __future__ import annotations
 
@@ -89,7 +93,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="paper",
                     help="paper (default: T=16384, V=4096, d=512, K=64), k1024, k16384, tiny, "
-                         "linear (hidden layer 512->2048, K=256, gamma=0.9)")
+                         "linear (hidden layer 512->2048, K=256, gamma=0.9); the other rows: "
+                         "forward, embedding, optim, cosine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -277,6 +282,127 @@ def run_linear(args, torch, dust, synth, w):
     return out
 
 
+def _time_calls(torch, fn, steps: int, warmup: int) -> float:
+    """ms per call of fn (work on torch's current stream), HIP events around
+    `steps` back-to-back calls after `warmup` untimed ones."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _row_line(args, metric, value, unit, ms, workload, roofline, extra=None):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": workload, "parallelism": "single GPU"}, "roofline": roofline}
+    out.update(extra or {})
+    return out
+
+
+def run_forward(args, torch, dust, synth):
+    """Perturbed forward of the hidden layer (512 -> 2048 over 8 x 2048 tokens),
+    8 draws per call: one bf16 product reused for every draw, the noise added
+    in the epilogue.  Bound by writing Y (4 B per token-column-draw)."""
+    T, d, N, nd = 16384, 512, 2048, 8
+    gen = torch.Generator().manual_seed(11)
+    X = (torch.randn(T, d, generator=gen) / d ** 0.5).to(torch.bfloat16).cuda()
+    W = (torch.randn(N, d, generator=gen) / d ** 0.5).to(torch.bfloat16).cuda()
+    Y = torch.empty((nd, T, N), dtype=torch.float32, device="cuda:0")
+    ms = _time_calls(torch, lambda: dust.perturbed_linear(X, W, sigma=0.01, seed=1, ndraw=nd,
+                                                          out=Y), args.steps, args.warmup)
+    ybytes = 4.0 * nd * T * N
+    in_bytes = 2.0 * (T * d + N * d)
+    gbs = (ybytes + in_bytes) / (ms / 1e3) / 1e9
+    slots = float(nd) * T * N * (SLOTS_PER_NORMAL_ERROR_ESTIMATE) / (ms / 1e3) / 1e12
+    roof = {"bound": "hbm", "kernel": "perturbed_linear_kernel (bf16 MFMA product + noise "
+            "epilogue)", "achieved": gbs, "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+            "frac": gbs * 1e9 / HBM_BYTES_PER_S, "traffic": None, "launch_ms": ms,
+            "valu_slots_tps": slots, "valu_frac": slots * 1e12 / VALU_SLOTS_PER_S,
+            "gemm_tflops": 2.0 * T * N * d / (ms / 1e3) / 1e12}
+    return _row_line(args, "token-draws/sec, perturbed forward y = W x + sigma a "
+                     f"(T={T}, d={d}, N={N})", T * nd / (ms / 1e3), "token-draws/s", ms,
+                     f"forward: bf16 X [{T},{d}], W [{N},{d}], {nd} draws per call, Y fp32",
+                     roof)
+
+
+def run_embedding(args, torch, dust, synth):
+    """Embedding estimate at the pages' shape: 16384 token ids (Zipf over a
+    4096-token vocabulary), error estimates of width 512."""
+    import numpy as np
+    T, N, vocab = 16384, 512, 4096
+    rng = np.random.default_rng(5)
+    ids = torch.from_numpy(synth.zipf_targets(rng, T, vocab)).cuda()
+    g = torch.from_numpy(rng.standard_normal((T, N)).astype(np.float32)).cuda()
+    G = torch.empty((vocab, N), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(dust._lib.load().dust_embedding_workspace_size(T, N, vocab), dtype=torch.uint8,
+                     device="cuda:0")
+    ms = _time_calls(torch, lambda: dust.embedding_grad(ids, g, vocab, out=G, workspace=ws),
+                     args.steps, args.warmup)
+    nbytes = 4.0 * T * N + 4.0 * vocab * N + 4.0 * T
+    gbs = nbytes / (ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "kernel": "rank/scan/scatter/gather (dust_embedding_grad)",
+            "achieved": gbs, "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
+            "frac": gbs * 1e9 / HBM_BYTES_PER_S, "traffic": None, "launch_ms": ms}
+    return _row_line(args, f"tokens/sec, embedding estimate G_E (T={T}, N={N}, vocab={vocab})",
+                     T / (ms / 1e3), "tokens/s", ms,
+                     f"embedding: {T} Zipf(1.1) ids over {vocab}, g fp32 [{T},{N}]", roof)
+
+
+def run_optim(args, torch, dust, synth):
+    """SGD + momentum and Adam steps over 2^24 fp32 parameters (the order of
+    the pages' 8 x 512 model)."""
+    n = 1 << 24
+    W = torch.randn(n, device="cuda:0")
+    G = torch.randn(n, device="cuda:0")
+    m = torch.zeros(n, device="cuda:0")
+    v = torch.zeros(n, device="cuda:0")
+    ms_sgd = _time_calls(torch, lambda: dust.sgd_momentum_(W, G, m, lr=1e-3, momentum=0.9),
+                         args.steps, args.warmup)
+    ms_adam = _time_calls(torch, lambda: dust.adam_(W, G, m, v, lr=1e-3, step=3),
+                          args.steps, args.warmup)
+    gbs_sgd = 16.0 * n / (ms_sgd / 1e3) / 1e9
+    gbs_adam = 28.0 * n / (ms_adam / 1e3) / 1e9
+    roof = {"bound": "hbm", "kernel": "adam_kernel", "achieved": gbs_adam,
+            "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s", "frac": gbs_adam * 1e9 / HBM_BYTES_PER_S,
+            "traffic": None, "launch_ms": ms_adam}
+    return _row_line(args, f"parameters/sec, Adam step on the estimate (n={n})",
+                     n / (ms_adam / 1e3), "params/s", ms_adam,
+                     f"optim: {n} fp32 parameters, 28 B (Adam) / 16 B (SGD) per parameter", roof,
+                     {"sgd_momentum": {"ms": ms_sgd, "achieved_gbs": gbs_sgd,
+                                       "frac": gbs_sgd * 1e9 / HBM_BYTES_PER_S}})
+
+
+def run_cosine(args, torch, dust, synth):
+    """The cosine-versus-population measurement at the paper shape: cosine of
+    g_hat (and of G_W) with the closed-form head gradient for K = 64 .. 16384,
+    and the fit of cos(K) = c_max / sqrt(1 + c/K)."""
+    from activation_perturbation_estimator_amd.cosine import cosine_sweep
+    w = synth.WORKLOADS["paper"]
+    z, y, X = synth.workload_inputs(w)
+    t0 = time.perf_counter()
+    res = cosine_sweep(z.cuda(), y.cuda(), X.cuda(), [64, 256, 1024, 4096, 16384],
+                       sigma=w.sigma, seed=1, seq_len=w.seq_len)
+    dt = time.perf_counter() - t0
+    return {"metric": "cosine of g_hat with softmax(z) - onehot(y) versus population K",
+            "value": res["fit_token"]["c"], "unit": "fitted c (law cos = c_max / sqrt(1 + c/K))",
+            "n_gpus": 1, "data": "synthetic", "dtype": "f32", "higher_is_better": False,
+            "config": {"workload": f"paper shape, T={w.T}, V={w.V}, sigma={w.sigma}, "
+                                   "K = 64, 256, 1024, 4096, 16384"},
+            "sweep": res, "predicted_c": w.V + 1, "wall_s": dt}
+
+
+ROWS = {"forward": run_forward, "embedding": run_embedding, "optim": run_optim,
+        "cosine": run_cosine}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -288,6 +414,9 @@ def main():
     import activation_perturbation_estimator_amd as dust
     from activation_perturbation_estimator_amd import synth
 
+    if args.workload in ROWS:
+        print(json.dumps(ROWS[args.workload](args, torch, dust, synth)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     run = run_linear if w.kind == "linear" else run_head
     print(json.dumps(run(args, torch, dust, synth, w)), flush=True)

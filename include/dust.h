@@ -212,14 +212,19 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
 
 /* Embedding layer (paper digest, section 2.2: a one-hot input turns the outer
  * product into a scatter-add): G_E[v,:] = sum over tokens t with ids[t] = v of
- * g_hat[t,:], summed in increasing t (deterministic; rows of unused ids are 0;
- * ids outside [0, vocab) are skipped).
+ * g_hat[t,:], the rows taken in increasing t (in blocks of 32 of the id-sorted
+ * order; deterministic, no atomics; rows of unused ids are 0; ids outside
+ * [0, vocab) are skipped).
  *   ids device [T] int32; g_hat device [T,N] fp32 (N % 4 == 0);
- *   G_E device [vocab,N] fp32 out; workspace >= dust_embedding_workspace_size. */
+ *   G_E device [vocab,N] fp32 out;
+ *   workspace >= dust_embedding_workspace_size(T, N, vocab) bytes (about
+ *   T/512 * vocab * 4 + T/32 * N * 8 + 8 T + 8 vocab).
+ * Requires T <= 2^22, vocab <= 2^24 and ceil(T/512) * vocab <= 2^31
+ * (DUST_ERR_UNSUPPORTED otherwise). */
 dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,
                                 int64_t vocab, float* G_E, void* workspace,
                                 size_t workspace_bytes, dust_stream_t s);
-size_t dust_embedding_workspace_size(int64_t T, int64_t vocab);
+size_t dust_embedding_workspace_size(int64_t T, int64_t N, int64_t vocab);
 
 /* Optimiser steps on a weight gradient (linlog explainer, experiment setup:
  * SGD with momentum; paper digest, section 3.3: Adam).  All arrays device fp32

@@ -13,16 +13,27 @@ from util import need_gpu, rel_l2
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,N,vocab", [(3000, 100, 257), (1, 4, 3), (2048, 8, 1),
-                                       (16384, 4096, 4096)])
-def test_embedding_grad(T, N, vocab):
+@pytest.mark.parametrize("T,N,vocab,layout", [(3000, 100, 257, "zipf"), (1, 4, 3, "zipf"),
+                                              (2048, 8, 1, "zipf"), (16384, 512, 4096, "zipf"),
+                                              (640, 12, 10, "blocks64"), (700, 8, 10, "blocks70"),
+                                              (300, 4, 5, "invalid")])
+def test_embedding_grad(T, N, vocab, layout):
+    """Zipf ids (a few ids own long runs that span many 64-position segments of
+    the sorted order), ids whose runs fill segments exactly or straddle them,
+    and inputs whose ids are all out of range."""
     dust = need_gpu()
     import torch
     rng = np.random.default_rng(T + N)
-    ids = synth.zipf_targets(rng, T, vocab)
-    if T > 10:
-        ids[::97] = -3          # out-of-range ids are skipped
-        ids[5::101] = vocab
+    if layout == "zipf":
+        ids = synth.zipf_targets(rng, T, vocab)
+        if T > 10:
+            ids[::97] = -3          # out-of-range ids are skipped
+            ids[5::101] = vocab
+    elif layout.startswith("blocks"):
+        run = int(layout[6:])
+        ids = rng.permutation(np.repeat(np.arange(vocab, dtype=np.int32), run))[:T].astype(np.int32)
+    else:
+        ids = np.full(T, vocab + 2, np.int32)
     g = rng.standard_normal((T, N)).astype(np.float32)
     gi, gg = torch.from_numpy(ids).cuda(), torch.from_numpy(g).cuda()
     a = dust.embedding_grad(gi, gg, vocab)
