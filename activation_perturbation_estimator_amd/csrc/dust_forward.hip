@@ -12,7 +12,8 @@
 // 16-byte rows without transposition.  fp32 operands are split into bf16
 // hi + lo and multiplied as hi*hi + lo*hi + hi*lo (fp32 accumulation).
 //
-// The product is formed once per tile; the epilogue stages the fp32 tile in
+// The product is formed once per tile (operands double buffered in LDS); the
+// epilogue stages the fp32 tile in
 // LDS so that each thread owns 4 consecutive columns of a row -- one Philox
 // block -- and then loops over the draws, adding sigma a and storing 16 bytes.
 #include "dust_device.hpp"
@@ -24,6 +25,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 fbf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float ff32x16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 fbf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float ff32x2_t;
+typedef __attribute__((ext_vector_type(4))) float ff32x4_t;
 typedef unsigned int fu32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFM = 128;        // tokens per workgroup tile
@@ -65,10 +67,7 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
   // operand stages during the product; the fp32 result tile afterwards
   extern __shared__ __attribute__((aligned(16))) uint16_t flds[];
   constexpr int kA = kFM * kFRow, kB = kFN * kFRow;
-  uint16_t* Ah = flds;
-  uint16_t* Al = flds + kA;
-  uint16_t* Bh = flds + 2 * kA;
-  uint16_t* Bl = flds + 2 * kA + kB;
+  constexpr int kStage = 2 * kA + 2 * kB;  // Ah, Al, Bh, Bl of one contraction step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -93,31 +92,47 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // Staging: 128 rows x 4 chunks of 8 contraction elements per operand.
-  for (int64_t kc = 0; kc < d; kc += kFK) {
+  // Staging: 128 rows x 4 chunks of 8 contraction elements per operand, two
+  // chunks per thread; the next step's chunks are fetched into registers
+  // while the matrix cores work on the current LDS stage (double buffered).
+  uint4 rah[2], ral[2], rbh[2], rbl[2];
+  auto fetch = [&](int64_t kc) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int chunk = tid + 256 * h;
       const int row = chunk >> 2, c = chunk & 3;
       const int64_t kk = kc + 8 * c;
-      uint4 hi, lo;
       // a row's chunk is either inside [0, d) or past its end (d % 8 == 0)
       if (kk < d) {
-        load_row8<kF32>(xa, (int)((row * d + kk) * kEs), hi, lo);
+        load_row8<kF32>(xa, (int)((row * d + kk) * kEs), rah[h], ral[h]);
+        load_row8<kF32>(wb, (int)((row * d + kk) * kEs), rbh[h], rbl[h]);
       } else {
-        hi = lo = make_uint4(0, 0, 0, 0);
+        rah[h] = ral[h] = rbh[h] = rbl[h] = make_uint4(0, 0, 0, 0);
       }
-      *reinterpret_cast<uint4*>(Ah + row * kFRow + 8 * c) = hi;
-      if constexpr (kF32) *reinterpret_cast<uint4*>(Al + row * kFRow + 8 * c) = lo;
-      if (kk < d) {
-        load_row8<kF32>(wb, (int)((row * d + kk) * kEs), hi, lo);
-      } else {
-        hi = lo = make_uint4(0, 0, 0, 0);
-      }
-      *reinterpret_cast<uint4*>(Bh + row * kFRow + 8 * c) = hi;
-      if constexpr (kF32) *reinterpret_cast<uint4*>(Bl + row * kFRow + 8 * c) = lo;
     }
-    __syncthreads();
+  };
+  auto stash = [&](int stage) {
+    uint16_t* Ah = flds + stage * kStage;
+    uint16_t* Al = Ah + kA;
+    uint16_t* Bh = Ah + 2 * kA;
+    uint16_t* Bl = Bh + kB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int chunk = tid + 256 * h;
+      const int row = chunk >> 2, c = chunk & 3;
+      *reinterpret_cast<uint4*>(Ah + row * kFRow + 8 * c) = rah[h];
+      *reinterpret_cast<uint4*>(Bh + row * kFRow + 8 * c) = rbh[h];
+      if constexpr (kF32) {
+        *reinterpret_cast<uint4*>(Al + row * kFRow + 8 * c) = ral[h];
+        *reinterpret_cast<uint4*>(Bl + row * kFRow + 8 * c) = rbl[h];
+      }
+    }
+  };
+  auto compute = [&](int stage) {
+    const uint16_t* Ah = flds + stage * kStage;
+    const uint16_t* Al = Ah + kA;
+    const uint16_t* Bh = Ah + 2 * kA;
+    const uint16_t* Bl = Bh + kB;
 #pragma unroll
     for (int ks = 0; ks < kFK; ks += 16) {
       const int koff = ks + 8 * (lane >> 5);
@@ -144,6 +159,16 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
           }
         }
     }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int nk = (int)((d + kFK - 1) / kFK);
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) fetch((int64_t)(i + 1) * kFK);
+    compute(i & 1);
+    if (i + 1 < nk) stash((i + 1) & 1);
     __syncthreads();
   }
 
@@ -182,12 +207,13 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
       if (t < T && j < nblk) {
         float a0, a1, a2, a3;
         normal4((uint32_t)j, (uint32_t)t, draw, stream, k0, k1, a0, a1, a2, a3);
-        float4 o;
+        ff32x4_t o;
         o.x = fmaf(sigma, a0, base[q].x);
         o.y = fmaf(sigma, a1, base[q].y);
         o.z = fmaf(sigma, a2, base[q].z);
         o.w = fmaf(sigma, a3, base[q].w);
-        *reinterpret_cast<float4*>(yk + t * N + 4 * j) = o;
+        // streaming store: Y is written once and is far larger than the caches
+        __builtin_nontemporal_store(o, reinterpret_cast<ff32x4_t*>(yk + t * N + 4 * j));
       }
     }
   }
@@ -198,7 +224,7 @@ hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int6
                                    uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s) {
   if (T == 0 || ndraw == 0) return hipSuccess;
   const int64_t tiles = ((T + kFM - 1) / kFM) * ((N + kFN - 1) / kFN);
-  const size_t operands = (size_t)2 * (2 * kFM * kFRow + 2 * kFN * kFRow);  // bytes, hi + lo
+  const size_t operands = (size_t)2 * 2 * (2 * kFM * kFRow + 2 * kFN * kFRow);  // 2 stages, hi + lo
   const size_t result = (size_t)kFM * (kFN + 4) * sizeof(float);
   const size_t lds = operands > result ? operands : result;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
