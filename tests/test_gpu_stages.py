@@ -105,7 +105,11 @@ def test_error_estimate(K, T, N, L, gamma):
 
 @pytest.mark.parametrize("T,N,d,bf16", [(600, 1000, 72, True), (600, 1000, 72, False),
                                          (1, 5, 3, False), (4097, 300, 129, True),
-                                         (2048, 512, 512, True), (31, 64, 64, False)])
+                                         (2048, 512, 512, True), (31, 64, 64, False),
+                                         # several token splits, ragged last split,
+                                         # N % 4 != 0, three column tiles
+                                         (9000, 257, 520, True), (20000, 384, 256, False),
+                                         (16417, 129, 264, True), (130, 4100, 8, True)])
 def test_outer_sum(T, N, d, bf16):
     dust = need_gpu()
     import torch
