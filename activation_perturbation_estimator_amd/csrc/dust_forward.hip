@@ -13,9 +13,11 @@
 // hi + lo and multiplied as hi*hi + lo*hi + hi*lo (fp32 accumulation).
 //
 // The product is formed once per tile (operands double buffered in LDS); the
-// epilogue stages the fp32 tile in
-// LDS so that each thread owns 4 consecutive columns of a row -- one Philox
-// block -- and then loops over the draws, adding sigma a and storing 16 bytes.
+// epilogue stages the fp32 tile in LDS, half a tile at a time, so that each
+// thread owns 4 consecutive columns of a token -- one Philox block -- and
+// writes that item for every draw (sigma a added, 16-byte streaming stores).
+// bf16 operands fit four workgroups per CU (40 KiB of LDS, <= 128 VGPRs), so
+// the product of one tile overlaps the stores of others.
 #include "dust_device.hpp"
 #include "dust_launch.hpp"
 
@@ -60,14 +62,14 @@ __device__ __forceinline__ void load_row8(__amdgpu_buffer_rsrc_t rs, int byte_of
 }
 
 template <bool kF32>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, kF32 ? 2 : 4)
 perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv, int64_t T,
                         int64_t N, int64_t d, float sigma, uint32_t draw0, int64_t ndraw,
                         uint32_t stream, uint32_t k0, uint32_t k1, float* __restrict__ Y) {
   // operand stages during the product; the fp32 result tile afterwards
   extern __shared__ __attribute__((aligned(16))) uint16_t flds[];
   constexpr int kA = kFM * kFRow, kB = kFN * kFRow;
-  constexpr int kStage = 2 * kA + 2 * kB;  // Ah, Al, Bh, Bl of one contraction step
+  constexpr int kStage = kF32 ? 2 * kA + 2 * kB : kA + kB;  // Ah, Bh (and Al, Bl) of one step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -113,9 +115,9 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
   };
   auto stash = [&](int stage) {
     uint16_t* Ah = flds + stage * kStage;
-    uint16_t* Al = Ah + kA;
-    uint16_t* Bh = Ah + 2 * kA;
-    uint16_t* Bl = Bh + kB;
+    uint16_t* Bh = Ah + (kF32 ? 2 : 1) * kA;
+    uint16_t* Al = Ah + kA;  // fp32 only
+    uint16_t* Bl = Bh + kB;  // fp32 only
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int chunk = tid + 256 * h;
@@ -130,9 +132,9 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
   };
   auto compute = [&](int stage) {
     const uint16_t* Ah = flds + stage * kStage;
-    const uint16_t* Al = Ah + kA;
-    const uint16_t* Bh = Ah + 2 * kA;
-    const uint16_t* Bl = Bh + kB;
+    const uint16_t* Bh = Ah + (kF32 ? 2 : 1) * kA;
+    const uint16_t* Al = Ah + kA;  // fp32 only
+    const uint16_t* Bl = Bh + kB;  // fp32 only
 #pragma unroll
     for (int ks = 0; ks < kFK; ks += 16) {
       const int koff = ks + 8 * (lane >> 5);
@@ -172,50 +174,51 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
     __syncthreads();
   }
 
-  // Result tile to LDS as fp32 [128][132] (padded rows).
+  // Result tile through LDS as fp32 [64][132] (padded rows), one half of the
+  // tokens at a time (the waves with wm = h own half h), so that the staging
+  // needs no more LDS than the operand stages.  Each thread then owns 8 items
+  // of the half (one token, 4 columns: one Philox block) and writes every draw
+  // of an item before moving on, so only one item's product is live.
   constexpr int kYRow = kFN + 4;
   float* tile = reinterpret_cast<float*>(flds);
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = wn * 64 + b * 32 + (lane & 31);
-        tile[row * kYRow + col] = acc[a][b][r];
-      }
-  __syncthreads();
-
-  // Epilogue: thread -> (row, group of 4 columns); 16 items per thread.
-  float4 base[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int item = tid + 256 * q;
-    const int row = item >> 5, grp = item & 31;
-    base[q] = *reinterpret_cast<const float4*>(tile + row * kYRow + 4 * grp);
-  }
   const int64_t nblk = N >> 2;
-  for (int64_t k = 0; k < ndraw; ++k) {
-    float* yk = Y + k * T * N;
-    const uint32_t draw = draw0 + (uint32_t)k;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = a * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int col = wn * 64 + b * 32 + (lane & 31);
+            tile[row * kYRow + col] = acc[a][b][r];
+          }
+    }
+    __syncthreads();
+    for (int q = 0; q < 8; ++q) {
       const int item = tid + 256 * q;
-      const int64_t t = t0 + (item >> 5);
+      const float4 base = *reinterpret_cast<const float4*>(tile + (item >> 5) * kYRow + 4 * (item & 31));
+      const int64_t t = t0 + 64 * h + (item >> 5);
       const int64_t j = (n0 >> 2) + (item & 31);
       if (t < T && j < nblk) {
-        float a0, a1, a2, a3;
-        normal4((uint32_t)j, (uint32_t)t, draw, stream, k0, k1, a0, a1, a2, a3);
-        ff32x4_t o;
-        o.x = fmaf(sigma, a0, base[q].x);
-        o.y = fmaf(sigma, a1, base[q].y);
-        o.z = fmaf(sigma, a2, base[q].z);
-        o.w = fmaf(sigma, a3, base[q].w);
-        // streaming store: Y is written once and is far larger than the caches
-        __builtin_nontemporal_store(o, reinterpret_cast<ff32x4_t*>(yk + t * N + 4 * j));
+        float* yt = Y + t * N + 4 * j;
+#pragma unroll 2
+        for (int64_t k = 0; k < ndraw; ++k) {
+          float a0, a1, a2, a3;
+          normal4((uint32_t)j, (uint32_t)t, draw0 + (uint32_t)k, stream, k0, k1, a0, a1, a2, a3);
+          ff32x4_t o;
+          o.x = fmaf(sigma, a0, base.x);
+          o.y = fmaf(sigma, a1, base.y);
+          o.z = fmaf(sigma, a2, base.z);
+          o.w = fmaf(sigma, a3, base.w);
+          // streaming store: Y is written once and is far larger than the caches
+          __builtin_nontemporal_store(o, reinterpret_cast<ff32x4_t*>(yt + k * T * N));
+        }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -224,8 +227,9 @@ hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int6
                                    uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s) {
   if (T == 0 || ndraw == 0) return hipSuccess;
   const int64_t tiles = ((T + kFM - 1) / kFM) * ((N + kFN - 1) / kFN);
-  const size_t operands = (size_t)2 * 2 * (2 * kFM * kFRow + 2 * kFN * kFRow);  // 2 stages, hi + lo
-  const size_t result = (size_t)kFM * (kFN + 4) * sizeof(float);
+  const size_t operands =
+      (size_t)2 * 2 * (bf16 ? 1 : 2) * (kFM * kFRow + kFN * kFRow);  // 2 stages (hi, + lo for fp32)
+  const size_t result = (size_t)(kFM / 2) * (kFN + 4) * sizeof(float);  // half the result tile
   const size_t lds = operands > result ? operands : result;
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   if (lds > 65536) {
