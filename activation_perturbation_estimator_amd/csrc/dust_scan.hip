@@ -27,17 +27,18 @@ __global__ void __launch_bounds__(256) centre_kernel(const float* __restrict__ x
 }
 
 // Segmented reverse scan r_t = c_t + gamma r_{t+1}.  One wave per (draw,
-// sequence); the sequence is walked from its end in tiles of 64 lanes x 8
-// elements.  Per tile: a coalesced load into LDS, a serial scan of each lane's
-// 8 elements with zero carry, a wave-wide suffix scan of the lanes' affine maps
-// x -> A + B x (B = gamma^8), and a second serial pass with the true carry.
-constexpr int kScanChunk = 8;
-constexpr int kScanTile = 64 * kScanChunk;
-
+// sequence); the sequence is walked from its end in tiles of 64 lanes x kE
+// elements (kE = 32 covers a 2048-token sequence in one tile, so each wave
+// issues all its loads at once).  Per tile: a coalesced load into LDS, a serial
+// scan of each lane's kE elements with zero carry, a wave-wide suffix scan of
+// the lanes' affine maps x -> A + B x (B = gamma^kE), and a second serial pass
+// with the true carry.
+template <int kE>
 __global__ void __launch_bounds__(256) reward_scan_kernel(const float* __restrict__ c, int64_t K,
                                                           int64_t T, int64_t L, float gamma,
                                                           float* __restrict__ r) {
-  __shared__ float buf[4][64 * (kScanChunk + 1)];
+  constexpr int kTile = 64 * kE;
+  __shared__ float buf[4][64 * (kE + 1)];  // rows of kE + 1: conflict-free lane-major reads
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t nseg = T / L;
@@ -48,31 +49,31 @@ __global__ void __launch_bounds__(256) reward_scan_kernel(const float* __restric
   const int64_t base = i * T + seg * L;
   float* sb = buf[wave];
 
-  float g8 = 1.f;
+  float gE = 1.f;
 #pragma unroll
-  for (int k = 0; k < kScanChunk; ++k) g8 *= gamma;
+  for (int k = 0; k < kE; ++k) gE *= gamma;
 
   float carry = 0.f;  // r at the first position after the current tile
-  for (int64_t tile_end = L; tile_end > 0; tile_end -= kScanTile) {
-    const int64_t tile_start = tile_end > kScanTile ? tile_end - kScanTile : 0;
+  for (int64_t tile_end = L; tile_end > 0; tile_end -= kTile) {
+    const int64_t tile_start = tile_end > kTile ? tile_end - kTile : 0;
     const int n = (int)(tile_end - tile_start);
-    const int off = kScanTile - n;  // a short tile is aligned to its end
+    const int off = kTile - n;  // a short tile is aligned to its end
 #pragma unroll
-    for (int k = 0; k < kScanChunk; ++k) {
+    for (int k = 0; k < kE; ++k) {
       const int e = k * 64 + lane;
       const float v = (e >= off) ? c[base + tile_start + (e - off)] : 0.f;
-      sb[(e / kScanChunk) * (kScanChunk + 1) + (e % kScanChunk)] = v;
+      sb[(e / kE) * (kE + 1) + (e % kE)] = v;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0);
-    float xv[kScanChunk];
+    float xv[kE];
 #pragma unroll
-    for (int k = 0; k < kScanChunk; ++k) xv[k] = sb[lane * (kScanChunk + 1) + k];
+    for (int k = 0; k < kE; ++k) xv[k] = sb[lane * (kE + 1) + k];
     // pass 1: this lane's chunk with zero carry
     float A = 0.f;
 #pragma unroll
-    for (int k = kScanChunk - 1; k >= 0; --k) A = fmaf(gamma, A, xv[k]);
-    float B = g8;
+    for (int k = kE - 1; k >= 0; --k) A = fmaf(gamma, A, xv[k]);
+    float B = gE;
     // suffix scan over lanes: (A,B) o (A',B') = (A + B A', B B')
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) {
@@ -89,17 +90,17 @@ __global__ void __launch_bounds__(256) reward_scan_kernel(const float* __restric
     // pass 2: true values
     float rho = cin;
 #pragma unroll
-    for (int k = kScanChunk - 1; k >= 0; --k) {
+    for (int k = kE - 1; k >= 0; --k) {
       rho = fmaf(gamma, rho, xv[k]);
-      sb[lane * (kScanChunk + 1) + k] = rho;
+      sb[lane * (kE + 1) + k] = rho;
     }
     carry = lane_value(R, 0);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int k = 0; k < kScanChunk; ++k) {
+    for (int k = 0; k < kE; ++k) {
       const int e = k * 64 + lane;
-      if (e >= off) r[base + tile_start + (e - off)] = sb[(e / kScanChunk) * (kScanChunk + 1) + (e % kScanChunk)];
+      if (e >= off) r[base + tile_start + (e - off)] = sb[(e / kE) * (kE + 1) + (e % kE)];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0);
@@ -127,8 +128,13 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
                               float* r, hipStream_t s) {
   const int64_t jobs = K * (T / L);
   if (jobs == 0) return hipSuccess;
-  hipLaunchKernelGGL(reward_scan_kernel, dim3((uint32_t)((jobs + 3) / 4)), dim3(256), 0, s, c, K,
-                     T, L, gamma, r);
+  const dim3 grid((uint32_t)((jobs + 3) / 4));
+  if (L >= 2048)
+    hipLaunchKernelGGL(reward_scan_kernel<32>, grid, dim3(256), 0, s, c, K, T, L, gamma, r);
+  else if (L >= 512)
+    hipLaunchKernelGGL(reward_scan_kernel<16>, grid, dim3(256), 0, s, c, K, T, L, gamma, r);
+  else
+    hipLaunchKernelGGL(reward_scan_kernel<8>, grid, dim3(256), 0, s, c, K, T, L, gamma, r);
   return hipGetLastError();
 }
 

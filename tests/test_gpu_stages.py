@@ -54,7 +54,8 @@ def test_centre(K, T):
 
 
 @pytest.mark.parametrize("K,T,L", [(3, 60, 1), (2, 70, 7), (2, 1024, 512), (2, 1026, 513),
-                                   (3, 4096, 2048), (1, 6000, 3000), (5, 600, 600)])
+                                   (3, 4096, 2048), (1, 6000, 3000), (5, 600, 600),
+                                   (2, 8200, 4100), (2, 2046, 1023)])
 @pytest.mark.parametrize("gamma", [0.0, 0.5, 0.9, 1.0])
 def test_reward_scan(K, T, L, gamma):
     dust = need_gpu()
