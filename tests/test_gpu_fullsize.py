@@ -1,8 +1,10 @@
 """Parity at the benchmark's full sizes, through the same call the benchmark
-times.  The oracle computes sampled rows of g_hat token by token (plus the
-sequence boundaries); G_W is checked on sampled rows against the fp64 outer
-product of the returned g_hat (the identity G_W = sum_t g_t x_t^T holds at any
-size), and its norm against the sampled-row relation."""
+times.  For the paper workload (the benchmark's) and the linear workload the
+oracle computes every row of g_hat (token by token, in parallel over tokens)
+and G_W is compared whole with the fp64 product of the oracle's g_hat and X.
+For K = 1024 and 16384 the oracle computes sampled rows (plus the sequence
+boundaries), and G_W is checked on sampled rows against the fp64 outer product
+of the returned g_hat (the identity G_W = sum_t g_t x_t^T holds at any size)."""
 import numpy as np
 import pytest
 
@@ -27,7 +29,24 @@ def _check_gw(g, X64, G, nrows=48):
     assert_parity(G[rows], ref, "G_W rows")
 
 
-@pytest.mark.parametrize("name,ntok", [("paper", 24), ("k1024", 6), ("k16384", 2)])
+def test_head_paper_every_row():
+    dust = need_gpu()
+    import torch
+    w = synth.WORKLOADS["paper"]
+    z, y, X = synth.workload_inputs(w)
+    print(f"[fullsize] paper, every row: T={w.T} V={w.V} d={w.d} K={w.K}", flush=True)
+    g, G = dust.head_estimate(z.cuda(), y.cuda(), X.cuda(), sigma=w.sigma, K=w.K,
+                              gamma=w.gamma, seed=w.philox_seed, seq_len=w.seq_len)
+    torch.cuda.synchronize()
+    g = g.cpu().numpy()
+    G = G.cpu().numpy()
+    ref = oracle.head_rows(synth.to_f64(z), y.numpy(), w.seq_len, w.sigma, w.K, w.gamma,
+                           w.philox_seed, np.arange(w.T))
+    assert_parity(g, ref, "g_hat, every row")
+    assert_parity(G, ref.T @ synth.to_f64(X), "G_W")
+
+
+@pytest.mark.parametrize("name,ntok", [("k1024", 6), ("k16384", 2)])
 def test_head_full_size(name, ntok):
     dust = need_gpu()
     import torch
@@ -63,8 +82,7 @@ def test_linear_full_size():
     torch.cuda.synchronize()
     g = g.cpu().numpy()
     G = G.cpu().numpy()
-    tok = _sample_tokens(w.T, w.seq_len, 24)
-    rows = oracle.linear_rows(c.double().numpy(), w.seq_len, w.V, w.sigma, w.gamma,
-                              w.philox_seed, tok)
-    assert_parity(g[tok], rows, "g_hat sampled rows")
-    _check_gw(g, synth.to_f64(X), G)
+    ref = oracle.linear_rows(c.double().numpy(), w.seq_len, w.V, w.sigma, w.gamma,
+                             w.philox_seed, np.arange(w.T))
+    assert_parity(g, ref, "g_hat, every row")
+    assert_parity(G, ref.T @ synth.to_f64(X), "G_W")
