@@ -207,6 +207,10 @@ def run_head(args, torch, dust, synth, w):
                        "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
                        "frac": achieved / peak, "traffic": measured_traffic(w.name),
                        "slots_per_normal": SLOTS_PER_NORMAL, "launch_ms": head_ms}
+    # the same kernel in HBM terms (algorithmic bytes: logits read once, g_hat written once)
+    head_bytes = w.T * w.V * (2.0 if w.bf16 else 4.0) + 4.0 * w.T + 4.0 * w.T * w.V
+    out["roofline"]["hbm_gbs"] = head_bytes / (head_ms / 1e3) / 1e9
+    out["roofline"]["hbm_frac"] = head_bytes / (head_ms / 1e3) / HBM_BYTES_PER_S
     out["stages_ms"] = {"head": stage[0], "error_estimate": stage[1], "outer_sum": stage[2]}
     out["outer_sum"] = outer_sum_fields(w, stage[2])
     if not args.no_cpu_baseline:
@@ -271,6 +275,10 @@ def run_linear(args, torch, dust, synth, w):
                        "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
                        "frac": achieved / peak, "traffic": None,
                        "slots_per_normal": SLOTS_PER_NORMAL_ERROR_ESTIMATE, "launch_ms": ee_ms}
+    # the accumulate pass in HBM terms too: it reads r [K,T] and writes g_hat [T,N]
+    acc_bytes = 4.0 * w.K * w.T + 4.0 * w.T * w.V
+    out["roofline"]["hbm_gbs"] = acc_bytes / (ee_ms / 1e3) / 1e9
+    out["roofline"]["hbm_frac"] = acc_bytes / (ee_ms / 1e3) / HBM_BYTES_PER_S
     out["reward_scan"] = {"bound": "hbm", "achieved": scan_bytes / (stage[0] / 1e3) / 1e9,
                           "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
                           "frac": scan_bytes / (stage[0] / 1e3) / HBM_BYTES_PER_S,
