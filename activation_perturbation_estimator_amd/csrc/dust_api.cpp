@@ -24,8 +24,9 @@ bool gamma_ok(float gamma) { return std::isfinite(gamma) && gamma >= 0.f && gamm
 bool dtype_ok(dust_dtype dt) { return dt == DUST_F32 || dt == DUST_BF16; }
 
 // Index products stay far below 2^62, the 32-bit counter words hold t and i,
-// and the outer product's 32-bit buffer offsets cover 256 rows of X^T.
+// and token positions of the G_W and embedding calls fit int32.
 constexpr int64_t kMaxT = (int64_t)1 << 22;          // calls that form G_W
+constexpr int64_t kMaxWidth = (int64_t)1 << 20;      // N and d of the calls that form G_W
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;     // calls that do not
 constexpr int64_t kMaxK = ((int64_t)1 << 31) - 64;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
@@ -120,7 +121,7 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
   if (!logits || !targets || !X || !g_hat || !G_W) return DUST_ERR_INVALID_ARG;
   if (!dtype_ok(logits_dt) || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
   if (T <= 0 || !width_ok(V) || d <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxT || d > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * V > kMaxElems || T * d > kMaxElems || K * T > kMaxElems || V * d > kMaxElems)
@@ -167,7 +168,7 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
                                  dust_stream_t s_, const dust_event_t* stage_events) {
   if (!X || !c || !g_hat || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
   if (T <= 0 || !width_ok(N) || d_in <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxT || d_in > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * N > kMaxElems || T * d_in > kMaxElems || K * T > kMaxElems || N * d_in > kMaxElems)
@@ -252,7 +253,7 @@ dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, i
                            size_t workspace_bytes, dust_stream_t s) {
   if (!g_hat || !X || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
   if (T <= 0 || N <= 0 || d <= 0) return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxT || N > kMaxWidth || d > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (T * N > kMaxElems || T * d > kMaxElems || N * d > kMaxElems) return DUST_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < dust_outer_sum_workspace_size(T, N, d))
     return DUST_ERR_WORKSPACE;

@@ -30,7 +30,8 @@
  *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens;
  *     T <= 2^22 per call for the calls that form G_W, DUST_ERR_UNSUPPORTED above),
  *     N = layer output width (N = V for the LM head, N % 4 == 0), d = layer
- *     input width, K draws.
+ *     input width (N, d <= 2^20 for the calls that form G_W, DUST_ERR_UNSUPPORTED
+ *     above), K draws.
  *
  * Noise convention (the pages fix only that the noise is standard normal and
  * independent per token; this is this library's counter-based stream, which

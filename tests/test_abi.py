@@ -129,3 +129,16 @@ def test_workspace_sizes_are_host_only_and_sane():
     assert lib.dust_head_workspace_size(16384, 4096, 512, 64, 0.9) >= ws + 64 * 16384 * 4
     assert lib.dust_linear_workspace_size(16384, 512, 2048, 256, 0.9) >= 256 * 16384 * 4
     assert lib.dust_outer_sum_workspace_size(16, 8, 8) > 0
+
+
+def test_size_limits_are_unsupported_not_invalid():
+    """Shapes beyond the documented limits of the G_W-forming calls (T <= 2^22;
+    N, d <= 2^20) are refused on the host with DUST_ERR_UNSUPPORTED."""
+    L, lib = _lib()
+    U = L.DUST_ERR_UNSUPPORTED
+    assert _head(lib, T=(1 << 22) + 128, L=128) == U
+    assert _head(lib, d=(1 << 20) + 1) == U
+    assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, (1 << 20) + 4, 4, FAKE, FAKE, 1 << 40, None) == U
+    assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, 4, (1 << 20) + 8, FAKE, FAKE, 1 << 40, None) == U
+    assert lib.dust_linear_estimate(FAKE, 1, FAKE, 4096, (1 << 20) + 8, 2048, 2048, 0.01, 8,
+                                    0.9, 1, 0, FAKE, FAKE, FAKE, 1 << 40, None, None) == U
