@@ -391,20 +391,26 @@ def run_optim(args, torch, dust, synth):
 def run_cosine(args, torch, dust, synth):
     """The cosine-versus-population measurement at the paper shape: cosine of
     g_hat (and of G_W) with the closed-form head gradient for K = 64 .. 16384,
-    and the fit of cos(K) = c_max / sqrt(1 + c/K)."""
+    and the fit of cos(K) = c_max / sqrt(1 + c/K), at the paper's sigma and at
+    two large ones where the Gaussian smoothing of the loss shows (the
+    first-order analysis predicts c = V + 1 and c_max -> 1 as sigma -> 0)."""
     from activation_perturbation_estimator_amd.cosine import cosine_sweep
     w = synth.WORKLOADS["paper"]
     z, y, X = synth.workload_inputs(w)
+    zc, yc, Xc = z.cuda(), y.cuda(), X.cuda()
     t0 = time.perf_counter()
-    res = cosine_sweep(z.cuda(), y.cuda(), X.cuda(), [64, 256, 1024, 4096, 16384],
-                       sigma=w.sigma, seed=1, seq_len=w.seq_len)
+    sweeps = {}
+    for sigma in (w.sigma, 1.0, 4.0):
+        sweeps[str(sigma)] = cosine_sweep(zc, yc, Xc, [64, 256, 1024, 4096, 16384], sigma=sigma,
+                                          seed=1, seq_len=w.seq_len)
     dt = time.perf_counter() - t0
+    res = sweeps[str(w.sigma)]
     return {"metric": "cosine of g_hat with softmax(z) - onehot(y) versus population K",
             "value": res["fit_token"]["c"], "unit": "fitted c (law cos = c_max / sqrt(1 + c/K))",
             "n_gpus": 1, "data": "synthetic", "dtype": "f32", "higher_is_better": False,
-            "config": {"workload": f"paper shape, T={w.T}, V={w.V}, sigma={w.sigma}, "
+            "config": {"workload": f"paper shape, T={w.T}, V={w.V}, sigma={w.sigma} (and 1, 4), "
                                    "K = 64, 256, 1024, 4096, 16384"},
-            "sweep": res, "predicted_c": w.V + 1, "wall_s": dt}
+            "sweep": res, "sweeps_by_sigma": sweeps, "predicted_c": w.V + 1, "wall_s": dt}
 
 
 ROWS = {"forward": run_forward, "embedding": run_embedding, "optim": run_optim,
