@@ -110,3 +110,32 @@ def test_out_of_range_targets_stay_in_bounds():
     assert not dust.check_targets(y.cuda(), 64)
     g, G, ell = _run(dust, z, y, X, sigma=0.1, K=4, gamma=0.0, seed=1, seq_len=8)
     assert np.isfinite(g).all() and np.isfinite(G).all()
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.9])
+def test_single_token(gamma):
+    # T = 1: one sequence of one token (the scan is the identity)
+    z, y, X = synth.head_inputs(1, 4096, 64, seed=11, bf16=True)
+    _check(z, y, X, sigma=0.02, K=64, gamma=gamma, seed=3, seq_len=1)
+
+
+def test_sequences_of_one_token_with_discount():
+    # gamma > 0 with seq_len = 1: every token is its own sequence (the unfused
+    # path with a scan that must restart at every token)
+    z, y, X = synth.head_inputs(64, 512, 16, seed=12)
+    _check(z, y, X, sigma=0.05, K=16, gamma=0.9, seed=2, seq_len=1)
+
+
+@pytest.mark.parametrize("zbf16,xbf16", [(False, True), (True, False)])
+def test_mixed_input_dtypes(zbf16, xbf16):
+    import torch
+    z, y, X = synth.head_inputs(96, 1000, 40, seed=13)
+    z = z.to(torch.bfloat16) if zbf16 else z
+    X = X.to(torch.bfloat16) if xbf16 else X
+    _check(z, y, X, sigma=0.05, K=9, gamma=0.0, seed=5, seq_len=96)
+
+
+@pytest.mark.parametrize("seed,stream", [(2**64 - 1, 0xFFFFFFFF), (0x0123456789ABCDEF, 7)])
+def test_extreme_seed_and_stream(seed, stream):
+    z, y, X = synth.head_inputs(40, 300, 12, seed=14)
+    _check(z, y, X, sigma=0.05, K=5, gamma=0.0, seed=seed, seq_len=40, stream=stream)

@@ -176,3 +176,14 @@ def test_cosine_law_fit():
     g16, G16 = oracle.head_estimate(z, y, X, T, sigma, 16, 0.0, 8)
     cw = lambda A, B: float(np.sum(A * B) / np.linalg.norm(A) / np.linalg.norm(B))
     assert cw(Gk, Gref) > cw(G16, Gref) and cw(Gk, Gref) > 0.9
+
+
+def test_one_token_sequences_make_the_discount_irrelevant():
+    # With seq_len = 1 every token is its own sequence: r_t = c_t whatever gamma,
+    # so the estimate equals the gamma = 0 one (paper digest, section 2.2: the
+    # discounted sum runs over later tokens of the same sequence only).
+    z, y, X = _inputs(24, 64, 8, seed=21)
+    g0, G0 = oracle.head_estimate(z, y, X, 24, 0.05, 6, 0.0, 3)
+    g1, G1 = oracle.head_estimate(z, y, X, 1, 0.05, 6, 0.9, 3)
+    assert np.allclose(g1, g0, rtol=1e-12, atol=1e-15)
+    assert np.allclose(G1, G0, rtol=1e-12, atol=1e-15)
