@@ -24,14 +24,19 @@ bool gamma_ok(float gamma) { return std::isfinite(gamma) && gamma >= 0.f && gamm
 bool dtype_ok(dust_dtype dt) { return dt == DUST_F32 || dt == DUST_BF16; }
 
 // Index products stay far below 2^62, the 32-bit counter words hold t and i,
-// and token positions of the G_W and embedding calls fit int32.
+// token positions of the G_W and embedding calls fit int32, and the kernels
+// that take one workgroup (at most 256 threads) per token keep their grid's
+// work-item count inside the 32 bits of a dispatch.
 constexpr int64_t kMaxT = (int64_t)1 << 22;          // calls that form G_W
 constexpr int64_t kMaxWidth = (int64_t)1 << 20;      // N and d of the calls that form G_W
-constexpr int64_t kMaxTokens = (int64_t)1 << 31;     // calls that do not
+constexpr int64_t kMaxTokens = ((int64_t)1 << 24) - 1;  // the other per-token calls
 constexpr int64_t kMaxK = ((int64_t)1 << 31) - 64;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 bool width_ok(int64_t N) { return N > 0 && N % 4 == 0 && N <= DUST_N_MAX; }
+
+// a * b <= lim for a, b >= 0, without forming a product that could overflow.
+bool prod_le(int64_t a, int64_t b, int64_t lim) { return b == 0 || a <= lim / b; }
 
 dust_status hip_status(hipError_t e) { return e == hipSuccess ? DUST_OK : DUST_ERR_HIP; }
 
@@ -126,6 +131,7 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * V > kMaxElems || T * d > kMaxElems || K * T > kMaxElems || V * d > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
+  if (!dust::outer_sum_supported(T, V, d)) return DUST_ERR_UNSUPPORTED;
   const HeadPlan plan = head_plan(T, V, d, K, gamma);
   if (workspace == nullptr || workspace_bytes < plan.total()) return DUST_ERR_WORKSPACE;
 
@@ -173,6 +179,7 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
   if (!sigma_ok(sigma) || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
   if (T * N > kMaxElems || T * d_in > kMaxElems || K * T > kMaxElems || N * d_in > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
+  if (!dust::outer_sum_supported(T, N, d_in)) return DUST_ERR_UNSUPPORTED;
   const LinearPlan plan = linear_plan(T, d_in, N, K, gamma);
   if (workspace == nullptr || workspace_bytes < plan.total()) return DUST_ERR_WORKSPACE;
 
@@ -203,7 +210,7 @@ dust_status dust_noise(uint64_t seed, uint32_t stream, int64_t draw0, int64_t nd
                        int64_t N, float* out, dust_stream_t s) {
   if (!out || ndraw < 0 || T < 0 || !width_ok(N) || draw0 < 0) return DUST_ERR_INVALID_ARG;
   if (draw0 + ndraw > ((int64_t)1 << 32) || T > ((int64_t)1 << 32)) return DUST_ERR_INVALID_ARG;
-  if (ndraw * T > kMaxElems / N) return DUST_ERR_UNSUPPORTED;
+  if (!prod_le(ndraw, T, kMaxElems / N)) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_noise_fill(out, ndraw, T, N, (uint32_t)draw0, stream, seed,
                                             as_stream(s)));
 }
@@ -219,31 +226,32 @@ dust_status dust_head_losses(const void* logits, dust_dtype logits_dt, const int
                              int64_t T, int64_t V, float sigma, int64_t K, uint64_t seed,
                              uint32_t stream, float* losses, dust_stream_t s) {
   if (!logits || !targets || !losses || !dtype_ok(logits_dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxTokens || !width_ok(V) || K <= 0 || K > kMaxK || !sigma_ok(sigma))
+  if (T <= 0 || !width_ok(V) || K <= 0 || K > kMaxK || !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
-  if (T * V > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxTokens || T * V > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_head_losses(logits, logits_dt == DUST_BF16, targets, T, V, sigma,
                                              K, stream, seed, losses, nullptr, as_stream(s)));
 }
 
 dust_status dust_centre(const float* x, int64_t K, int64_t T, float* c, dust_stream_t s) {
-  if (!x || !c || K <= 0 || T <= 0 || K * T > kMaxElems) return DUST_ERR_INVALID_ARG;
+  if (!x || !c || K <= 0 || T <= 0) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxTokens || !prod_le(K, T, kMaxElems)) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_centre(x, K, T, c, as_stream(s)));
 }
 
 dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_len, float gamma,
                              float* r, dust_stream_t s) {
-  if (!c || !r || K <= 0 || T <= 0 || K * T > kMaxElems) return DUST_ERR_INVALID_ARG;
+  if (!c || !r || K <= 0 || T <= 0) return DUST_ERR_INVALID_ARG;
   if (seq_len <= 0 || T % seq_len != 0 || !gamma_ok(gamma)) return DUST_ERR_INVALID_ARG;
+  if (!prod_le(K, T, kMaxElems)) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_reward_scan(c, K, T, seq_len, gamma, r, as_stream(s)));
 }
 
 dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
                                 uint64_t seed, uint32_t stream, float* g_hat, dust_stream_t s) {
-  if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || T > kMaxTokens || !width_ok(N) ||
-      !sigma_ok(sigma))
+  if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || !width_ok(N) || !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
-  if (T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxTokens || T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
   return hip_status(
       dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, g_hat, as_stream(s)));
 }
@@ -255,6 +263,7 @@ dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, i
   if (T <= 0 || N <= 0 || d <= 0) return DUST_ERR_INVALID_ARG;
   if (T > kMaxT || N > kMaxWidth || d > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (T * N > kMaxElems || T * d > kMaxElems || N * d > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  if (!dust::outer_sum_supported(T, N, d)) return DUST_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < dust_outer_sum_workspace_size(T, N, d))
     return DUST_ERR_WORKSPACE;
   return hip_status(dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, N, d, G_W,
@@ -266,9 +275,9 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
                                   uint32_t stream, int64_t draw0, int64_t ndraw, float* Y,
                                   dust_stream_t s) {
   if (!X || !W || !Y || !dtype_ok(dt)) return DUST_ERR_INVALID_ARG;
-  if (T <= 0 || T > kMaxTokens || N <= 0 || N % 4 != 0 || d <= 0 || d % 8 != 0)
-    return DUST_ERR_INVALID_ARG;
-  if (N > ((int64_t)1 << 20) || d > ((int64_t)1 << 20)) return DUST_ERR_UNSUPPORTED;
+  if (T <= 0 || N <= 0 || N % 4 != 0 || d <= 0 || d % 8 != 0) return DUST_ERR_INVALID_ARG;
+  if (T > kMaxTokens || N > kMaxWidth || d > kMaxWidth) return DUST_ERR_UNSUPPORTED;
+  if (!dust::perturbed_linear_supported(T, N)) return DUST_ERR_UNSUPPORTED;
   if (!sigma_ok(sigma) || draw0 < 0 || ndraw < 0 || draw0 + ndraw > ((int64_t)1 << 32))
     return DUST_ERR_INVALID_ARG;
   if (ndraw * T > kMaxElems / N) return DUST_ERR_UNSUPPORTED;
@@ -289,7 +298,8 @@ dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t 
                                 size_t workspace_bytes, dust_stream_t s) {
   if (!ids || !g_hat || !G_E || T < 0 || N <= 0 || N % 4 != 0 || vocab <= 0)
     return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT || vocab > ((int64_t)1 << 24) || T * N > kMaxElems || vocab * N > kMaxElems)
+  if (T > kMaxT || N > kMaxWidth || vocab > ((int64_t)1 << 24) || T * N > kMaxElems ||
+      vocab * N > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
   if (((T + 511) / 512) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < dust_embedding_workspace_size(T, N, vocab))
@@ -325,7 +335,7 @@ dust_status dust_adam(float* W, const float* G, float* m, float* v, int64_t n, f
 dust_status dust_ce_grad(const void* logits, dust_dtype dt, const int32_t* targets, int64_t T,
                          int64_t V, float* out, dust_stream_t s) {
   if (!logits || !targets || !out || !dtype_ok(dt) || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;
-  if (T > kMaxTokens || T * V > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  if (T > kMaxTokens || !prod_le(T, V, kMaxElems)) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_ce_grad(logits, dt == DUST_BF16, targets, T, V, out,
                                          as_stream(s)));
 }

@@ -222,6 +222,11 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
   }
 }
 
+bool perturbed_linear_supported(int64_t T, int64_t N) {
+  // one workgroup of 256 threads per output tile: the grid must fit 32 bits
+  return ((T + kFM - 1) / kFM) * ((N + kFN - 1) / kFN) < ((int64_t)1 << 24);
+}
+
 hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int64_t T, int64_t N,
                                    int64_t d, float sigma, uint64_t seed, uint32_t stream,
                                    uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s) {

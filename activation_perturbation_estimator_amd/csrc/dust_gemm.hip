@@ -110,40 +110,41 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
 
 // Token-major copies for the operands the main kernel cannot read in place:
 // X as bf16 planes [T][dp] (dp = d rounded up to 8; hi and, for fp32 X, lo),
-// zero in the padding columns.  One thread per 8 columns of a row.
+// zero in the padding columns.  One thread per 8 columns of a row, grid-stride.
 template <bool kXF32>
 __global__ void __launch_bounds__(256) x_planes_kernel(const void* __restrict__ Xv, int64_t T,
                                                        int64_t d, int64_t dp,
                                                        uint16_t* __restrict__ hi,
                                                        uint16_t* __restrict__ lo) {
   const int64_t per_row = dp / 8;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * per_row) return;
-  const int64_t t = i / per_row, c0 = (i % per_row) * 8;
-  float v[8];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T * per_row; i += stride) {
+    const int64_t t = i / per_row, c0 = (i % per_row) * 8;
+    float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t c = c0 + e;
-    v[e] = 0.f;
-    if (c < d) {
-      if constexpr (kXF32) v[e] = reinterpret_cast<const float*>(Xv)[t * d + c];
-      else v[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + c] << 16);
+    for (int e = 0; e < 8; ++e) {
+      const int64_t c = c0 + e;
+      v[e] = 0.f;
+      if (c < d) {
+        if constexpr (kXF32) v[e] = reinterpret_cast<const float*>(Xv)[t * d + c];
+        else v[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + c] << 16);
+      }
     }
+    uint4 h, l;
+    if constexpr (kXF32) {
+      split2(v[0], v[1], h.x, l.x);
+      split2(v[2], v[3], h.y, l.y);
+      split2(v[4], v[5], h.z, l.z);
+      split2(v[6], v[7], h.w, l.w);
+      *reinterpret_cast<uint4*>(lo + t * dp + c0) = l;
+    } else {
+      h.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+      h.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
+      h.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
+      h.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint4*>(hi + t * dp + c0) = h;
   }
-  uint4 h, l;
-  if constexpr (kXF32) {
-    split2(v[0], v[1], h.x, l.x);
-    split2(v[2], v[3], h.y, l.y);
-    split2(v[4], v[5], h.z, l.z);
-    split2(v[6], v[7], h.w, l.w);
-    *reinterpret_cast<uint4*>(lo + t * dp + c0) = l;
-  } else {
-    h.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
-    h.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
-    h.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
-    h.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
-  }
-  *reinterpret_cast<uint4*>(hi + t * dp + c0) = h;
 }
 
 // g [T][N] -> [T][Np] (Np = N rounded up to 4), zero padding; only for N % 4 != 0.
@@ -449,6 +450,14 @@ static WsLayout ws_layout(int64_t T, int64_t N, int64_t d) {
   return w;
 }
 
+bool outer_sum_supported(int64_t T, int64_t N, int64_t d) {
+  // one workgroup per (tile, split): the grid's work-items must fit 32 bits
+  const GemmGeom a = plan_t<false>(T, N, d), b = plan_t<true>(T, N, d);
+  const int64_t na = a.groups_per_xcd * kXcds * a.tiles_n;
+  const int64_t nb = b.groups_per_xcd * kXcds * b.tiles_n;
+  return (na > nb ? na : nb) < ((int64_t)1 << 24);
+}
+
 size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d) {
   const WsLayout w = ws_layout(T, N, d);
   return 2 * w.plane + w.gpad + w.part;
@@ -477,7 +486,7 @@ hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t 
   const uint16_t* xh = reinterpret_cast<const uint16_t*>(X);
   if (!x_bf16 || d % 8 != 0) {
     const int64_t n = T * (geo.dp / 8);
-    const dim3 grid((uint32_t)((n + 255) / 256));
+    const dim3 grid((uint32_t)(n / 256 < 16384 ? n / 256 + 1 : 16384));
     if (x_bf16)
       hipLaunchKernelGGL(x_planes_kernel<false>, grid, dim3(256), 0, s, X, T, d, geo.dp, ph, nullptr);
     else

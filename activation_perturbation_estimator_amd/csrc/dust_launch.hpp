@@ -42,10 +42,12 @@ hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N
 
 // Outer-product sum G = g^T X on the matrix cores.
 size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d);
+bool outer_sum_supported(int64_t T, int64_t N, int64_t d);  // the launch grid fits
 hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
                             int64_t d, float* G, void* workspace, hipStream_t s);
 
 // Perturbed forward of a linear layer: Y[k] = X W^T + sigma a^(draw0+k).
+bool perturbed_linear_supported(int64_t T, int64_t N);  // the launch grid fits
 hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int64_t T, int64_t N,
                                    int64_t d, float sigma, uint64_t seed, uint32_t stream,
                                    uint32_t draw0, int64_t ndraw, float* Y, hipStream_t s);

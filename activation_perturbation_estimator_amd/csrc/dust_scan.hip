@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(256) centre_kernel(const float* __restrict__ x
 }
 
 // Segmented reverse scan r_t = c_t + gamma r_{t+1}.  One wave per (draw,
-// sequence); the sequence is walked from its end in tiles of 64 lanes x kE
+// sequence) job, the waves striding over the jobs; the sequence is walked from its end in tiles of 64 lanes x kE
 // elements (kE = 32 covers a 2048-token sequence in one tile, so each wave
 // issues all its loads at once).  Per tile: a coalesced load into LDS, a serial
 // scan of each lane's kE elements with zero carry, a wave-wide suffix scan of
@@ -42,68 +42,69 @@ __global__ void __launch_bounds__(256) reward_scan_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t nseg = T / L;
-  const int64_t job = (int64_t)blockIdx.x * 4 + wave;
-  if (job >= K * nseg) return;  // whole wave leaves; no workgroup barrier follows
-  const int64_t i = job / nseg;
-  const int64_t seg = job - i * nseg;
-  const int64_t base = i * T + seg * L;
   float* sb = buf[wave];
-
   float gE = 1.f;
 #pragma unroll
   for (int k = 0; k < kE; ++k) gE *= gamma;
 
-  float carry = 0.f;  // r at the first position after the current tile
-  for (int64_t tile_end = L; tile_end > 0; tile_end -= kTile) {
-    const int64_t tile_start = tile_end > kTile ? tile_end - kTile : 0;
-    const int n = (int)(tile_end - tile_start);
-    const int off = kTile - n;  // a short tile is aligned to its end
+  // Waves stride over the jobs; a wave leaves on its own (no workgroup barrier).
+  const int64_t njobs = K * nseg;
+  for (int64_t job = (int64_t)blockIdx.x * 4 + wave; job < njobs; job += (int64_t)gridDim.x * 4) {
+    const int64_t i = job / nseg;
+    const int64_t seg = job - i * nseg;
+    const int64_t base = i * T + seg * L;
+    float carry = 0.f;  // r at the first position after the current tile
+    for (int64_t tile_end = L; tile_end > 0; tile_end -= kTile) {
+      const int64_t tile_start = tile_end > kTile ? tile_end - kTile : 0;
+      const int n = (int)(tile_end - tile_start);
+      const int off = kTile - n;  // a short tile is aligned to its end
 #pragma unroll
-    for (int k = 0; k < kE; ++k) {
-      const int e = k * 64 + lane;
-      const float v = (e >= off) ? c[base + tile_start + (e - off)] : 0.f;
-      sb[(e / kE) * (kE + 1) + (e % kE)] = v;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
-    float xv[kE];
-#pragma unroll
-    for (int k = 0; k < kE; ++k) xv[k] = sb[lane * (kE + 1) + k];
-    // pass 1: this lane's chunk with zero carry
-    float A = 0.f;
-#pragma unroll
-    for (int k = kE - 1; k >= 0; --k) A = fmaf(gamma, A, xv[k]);
-    float B = gE;
-    // suffix scan over lanes: (A,B) o (A',B') = (A + B A', B B')
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const float An = __shfl_down(A, sh, 64);
-      const float Bn = __shfl_down(B, sh, 64);
-      if (lane + sh < 64) {
-        A = fmaf(B, An, A);
-        B = B * Bn;
+      for (int k = 0; k < kE; ++k) {
+        const int e = k * 64 + lane;
+        const float v = (e >= off) ? c[base + tile_start + (e - off)] : 0.f;
+        sb[(e / kE) * (kE + 1) + (e % kE)] = v;
       }
-    }
-    const float R = fmaf(B, carry, A);            // r at this lane's first element
-    float cin = __shfl_down(R, 1, 64);            // r at the next lane's first element
-    if (lane == 63) cin = carry;
-    // pass 2: true values
-    float rho = cin;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+      float xv[kE];
 #pragma unroll
-    for (int k = kE - 1; k >= 0; --k) {
-      rho = fmaf(gamma, rho, xv[k]);
-      sb[lane * (kE + 1) + k] = rho;
-    }
-    carry = lane_value(R, 0);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+      for (int k = 0; k < kE; ++k) xv[k] = sb[lane * (kE + 1) + k];
+      // pass 1: this lane's chunk with zero carry
+      float A = 0.f;
 #pragma unroll
-    for (int k = 0; k < kE; ++k) {
-      const int e = k * 64 + lane;
-      if (e >= off) r[base + tile_start + (e - off)] = sb[(e / kE) * (kE + 1) + (e % kE)];
+      for (int k = kE - 1; k >= 0; --k) A = fmaf(gamma, A, xv[k]);
+      float B = gE;
+      // suffix scan over lanes: (A,B) o (A',B') = (A + B A', B B')
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const float An = __shfl_down(A, sh, 64);
+        const float Bn = __shfl_down(B, sh, 64);
+        if (lane + sh < 64) {
+          A = fmaf(B, An, A);
+          B = B * Bn;
+        }
+      }
+      const float R = fmaf(B, carry, A);            // r at this lane's first element
+      float cin = __shfl_down(R, 1, 64);            // r at the next lane's first element
+      if (lane == 63) cin = carry;
+      // pass 2: true values
+      float rho = cin;
+#pragma unroll
+      for (int k = kE - 1; k >= 0; --k) {
+        rho = fmaf(gamma, rho, xv[k]);
+        sb[lane * (kE + 1) + k] = rho;
+      }
+      carry = lane_value(R, 0);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int k = 0; k < kE; ++k) {
+        const int e = k * 64 + lane;
+        if (e >= off) r[base + tile_start + (e - off)] = sb[(e / kE) * (kE + 1) + (e % kE)];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 
@@ -128,7 +129,7 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
                               float* r, hipStream_t s) {
   const int64_t jobs = K * (T / L);
   if (jobs == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((jobs + 3) / 4));
+  const dim3 grid((uint32_t)((jobs + 3) / 4 < 65536 ? (jobs + 3) / 4 : 65536));
   if (L >= 2048)
     hipLaunchKernelGGL(reward_scan_kernel<32>, grid, dim3(256), 0, s, c, K, T, L, gamma, r);
   else if (L >= 512)

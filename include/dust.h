@@ -27,11 +27,17 @@
  *     has no effect.  Launch failures are reported as DUST_ERR_HIP.  Nothing is
  *     thrown across this interface.
  *   - Layouts are row-major; [A,B] means A rows of B contiguous elements.
- *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens;
- *     T <= 2^22 per call for the calls that form G_W, DUST_ERR_UNSUPPORTED above),
+ *   - T tokens (T % seq_len == 0, sequences of seq_len consecutive tokens),
  *     N = layer output width (N = V for the LM head, N % 4 == 0), d = layer
- *     input width (N, d <= 2^20 for the calls that form G_W, DUST_ERR_UNSUPPORTED
- *     above), K draws.
+ *     input width, K draws.
+ *   - Size limits (DUST_ERR_UNSUPPORTED beyond them): the calls that form G_W
+ *     take T <= 2^22 and N, d <= 2^20, with at most 2^24 - 1 workgroups in the
+ *     outer-product grid: ceil(N/128) x ceil(d/256) tiles of G_W times the
+ *     token splits, where one split holds at most about 2^29 / (max(N, d/2) + 128)
+ *     tokens (at T = 2^22 this binds from N = d = 2^16 up); the per-token
+ *     stages (dust_head_losses, dust_centre, dust_error_estimate,
+ *     dust_perturbed_linear, dust_ce_grad) take T < 2^24; element counts of
+ *     every array stay <= 2^40.
  *
  * Noise convention (the pages fix only that the noise is standard normal and
  * independent per token; this is this library's counter-based stream, which
@@ -205,7 +211,8 @@ size_t dust_outer_sum_workspace_size(int64_t T, int64_t N, int64_t d);
  *   (bf16 operands multiply exactly; fp32 operands are split into bf16 hi + lo)
  *   Y device [ndraw,T,N] fp32 out
  * Requires N % 4 == 0, d % 8 == 0, 0 < sigma <= DUST_SIGMA_MAX (sigma = 0 is
- * rejected: use a plain GEMM), T <= 2^31, N, d <= 2^20. */
+ * rejected: use a plain GEMM), T < 2^24, N, d <= 2^20 and fewer than 2^24
+ * output tiles of 128 x 128 (DUST_ERR_UNSUPPORTED otherwise). */
 dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, int64_t T,
                                   int64_t d, int64_t N, float sigma, uint64_t seed,
                                   uint32_t stream, int64_t draw0, int64_t ndraw, float* Y,
@@ -220,7 +227,7 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
  *   G_E device [vocab,N] fp32 out;
  *   workspace >= dust_embedding_workspace_size(T, N, vocab) bytes (about
  *   T/512 * vocab * 4 + T/32 * N * 8 + 8 T + 8 vocab).
- * Requires T <= 2^22, vocab <= 2^24 and ceil(T/512) * vocab <= 2^31
+ * Requires T <= 2^22, N <= 2^20, vocab <= 2^24 and ceil(T/512) * vocab <= 2^31
  * (DUST_ERR_UNSUPPORTED otherwise). */
 dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,
                                 int64_t vocab, float* G_E, void* workspace,

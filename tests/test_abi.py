@@ -142,3 +142,29 @@ def test_size_limits_are_unsupported_not_invalid():
     assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, 4, (1 << 20) + 8, FAKE, FAKE, 1 << 40, None) == U
     assert lib.dust_linear_estimate(FAKE, 1, FAKE, 4096, (1 << 20) + 8, 2048, 2048, 0.01, 8,
                                     0.9, 1, 0, FAKE, FAKE, FAKE, 1 << 40, None, None) == U
+
+
+def test_grid_and_overflow_limits():
+    """Sizes whose launch grid would not fit a dispatch's 32-bit work-item count,
+    or whose element counts would overflow a 64-bit product, are refused on the
+    host (DUST_ERR_UNSUPPORTED) instead of reaching a kernel."""
+    L, lib = _lib()
+    U = L.DUST_ERR_UNSUPPORTED
+    big = 1 << 24                                      # one workgroup per token: T < 2^24
+    assert lib.dust_error_estimate(FAKE, 2, big, 4, 0.1, 1, 0, FAKE, None) == U
+    assert lib.dust_head_losses(FAKE, 0, FAKE, big, 4, 0.1, 2, 1, 0, FAKE, None) == U
+    assert lib.dust_centre(FAKE, 1, big, FAKE, None) == U
+    assert lib.dust_ce_grad(FAKE, 0, FAKE, big, 4, FAKE, None) == U
+    assert lib.dust_perturbed_linear(FAKE, FAKE, 1, big, 8, 8, 0.1, 1, 0, 0, 1, FAKE, None) == U
+    # products that would overflow int64 if formed directly
+    assert lib.dust_centre(FAKE, 1 << 40, 1 << 23, FAKE, None) == U
+    assert lib.dust_reward_scan(FAKE, 1 << 62, 4, 4, 0.5, FAKE, None) == U
+    assert lib.dust_ce_grad(FAKE, 0, FAKE, 8, 1 << 62, FAKE, None) == U
+    assert lib.dust_noise(1, 0, 0, 1 << 32, 1 << 32, 4, FAKE, None) == U
+    assert lib.dust_embedding_grad(FAKE, FAKE, 8, 1 << 60, 8, FAKE, FAKE, 1 << 40, None) == U
+    # perturbed forward: more than 2^24 - 1 tiles of 128 x 128 outputs
+    assert lib.dust_perturbed_linear(FAKE, FAKE, 1, 1 << 23, 8, 1 << 15, 0.1, 1, 0, 0, 1,
+                                     FAKE, None) == U
+    # outer product at widths whose tile grid alone exceeds 2^24 workgroups
+    assert lib.dust_outer_sum(FAKE, FAKE, 1, 1024, 1 << 20, 1 << 20, FAKE, FAKE, 1 << 62,
+                              None) == U

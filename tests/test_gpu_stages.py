@@ -136,3 +136,31 @@ def test_check_targets():
     assert not dust.check_targets(y, 100)
     y[517] = -1
     assert not dust.check_targets(y, 100)
+
+
+def test_reward_scan_more_jobs_than_grid():
+    """K * T / L = 524288 (draw, sequence) jobs: more than the scan's grid of
+    65536 workgroups x 4 waves, so every wave walks several jobs."""
+    dust = need_gpu()
+    import torch
+    K, T, L = 4096, 256, 2
+    c = np.random.default_rng(11).standard_normal((K, T)).astype(np.float32)
+    r = dust.reward_scan(_cuda(torch.from_numpy(c)), seq_len=L, gamma=0.75)
+    torch.cuda.synchronize()
+    ref = oracle.reward_scan(c.astype(np.float64), L, 0.75)
+    assert rel_l2(r.cpu().numpy(), ref) <= 1e-5
+
+
+def test_outer_sum_planes_grid_stride():
+    """fp32 X with T * d / 8 above the plane pass's 16384 x 256 threads, so the
+    pass strides; d = 520 also leaves a ragged column tile."""
+    dust = need_gpu()
+    import torch
+    T, N, d = 65536, 32, 520
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((T, N)).astype(np.float32)
+    Xf = rng.standard_normal((T, d)).astype(np.float32)
+    G = dust.outer_sum(_cuda(torch.from_numpy(g)), _cuda(torch.from_numpy(Xf)))
+    torch.cuda.synchronize()
+    ref = oracle.outer_sum(g.astype(np.float64), Xf.astype(np.float64))
+    assert_parity(G.cpu().numpy(), ref, "G_W")
