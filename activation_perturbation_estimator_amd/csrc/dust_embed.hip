@@ -16,13 +16,15 @@
 //   2. row_offsets     : per id, the exclusive prefix of the chunk counts and
 //                        the id's total.
 //   3. id_scan         : exclusive scan of the totals (one workgroup).
-//   4. scatter_kernel  : order[start[id] + chunk offset + rank] = t.
-//   5. segment_kernel  : one workgroup per segment of the sorted order: the
-//                        sum of each run of equal ids in it, written to G_E
-//                        when the run is the id's whole range, else kept as a
-//                        partial (at most the first and the last run).
-//   6. finish_kernel   : per id, zero rows for absent ids and the in-order sum
-//                        of the partials for ids that span segments.
+//   4. scatter_kernel  : order[start[id] + chunk offset + rank] = t, with the
+//                        id (and whether its range fits one segment) beside it.
+//   5. segment_kernel  : one wave per segment of the sorted order and block of
+//                        256 columns: the sum of each run of equal ids in it,
+//                        written to G_E when the run is the id's whole range,
+//                        else kept as a partial (at most the first and the
+//                        last run).
+//   6. finish_kernel   : per id, the zero row of an absent id, or the in-order
+//                        sum of the partials of an id that spans segments.
 // Ids outside [0, vocab) are skipped.
 #include "dust_device.hpp"
 #include "dust_launch.hpp"
@@ -31,51 +33,77 @@ namespace dust {
 
 constexpr int kChunk = 512;   // tokens per rank workgroup (a power of two)
 constexpr int kSeg = 32;      // sorted positions per segment workgroup
+constexpr int kSegCols = 64;  // float4 columns per segment workgroup (one wave)
+constexpr int kFinishBatch = 32;  // partial rows in flight when an id's partials are summed
+constexpr int kRankRowMax = 8192;  // vocabularies whose counts rows the rank pass writes whole
 
-// The chunk's (id, position) pairs are sorted in LDS (bitonic network, keys
-// id * 2^32 + position, out-of-range ids last); a token's rank is its sorted
-// position minus the first sorted position of its id, and the last token of
-// each run records the run length as the chunk's count of that id.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The chunk's (id, position) pairs are sorted by a bitonic network (keys
+// id * 2^32 + position, out-of-range ids last): the stages whose partners sit
+// in the same wave exchange keys by shuffles, the others through LDS (two
+// buffers, one barrier per stage).  A token's rank is its sorted position
+// minus the first sorted position of its id, and the last token of each run
+// holds the run length, the chunk's count of that id.  With full_row
+// (vocab <= kRankRowMax) the counts are gathered in LDS and the workgroup
+// writes its whole row of counts, zeros included; otherwise only present ids
+// are written and the row must have been cleared before.
 __global__ void __launch_bounds__(kChunk) rank_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                       int64_t vocab, int32_t* __restrict__ rank,
-                                                      int32_t* __restrict__ counts) {
-  __shared__ uint64_t key[kChunk];
+                                                      int32_t* __restrict__ counts, int full_row) {
+  __shared__ uint64_t key[2][kChunk];
+  __shared__ int32_t cnt[kRankRowMax];
   const int64_t c = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t t = c * kChunk + tid;
+  if (full_row)
+    for (int v = tid; v < vocab; v += kChunk) cnt[v] = 0;  // ordered by the barriers below
   uint64_t k = ~0ull;
   if (t < T) {
     const int32_t v = ids[t];
     if (v >= 0 && v < vocab) k = ((uint64_t)(uint32_t)v << 32) | (uint32_t)tid;
   }
-  key[tid] = k;
+  int buf = 0;
   for (int size = 2; size <= kChunk; size <<= 1)
     for (int j = size >> 1; j > 0; j >>= 1) {
-      __syncthreads();
-      const int partner = tid ^ j;
-      if (partner > tid) {
-        const uint64_t a = key[tid], b = key[partner];
-        const bool ascending = (tid & size) == 0;
-        if ((a > b) == ascending) {
-          key[tid] = b;
-          key[partner] = a;
-        }
+      uint64_t other;
+      if (j >= 64) {
+        key[buf][tid] = k;
+        __syncthreads();
+        other = key[buf][tid ^ j];
+        buf ^= 1;
+      } else {
+        other = shfl_xor64(k, j);
       }
+      const bool keep_min = ((tid & j) == 0) == ((tid & size) == 0);
+      k = keep_min ? (other < k ? other : k) : (other < k ? k : other);
     }
+  key[buf][tid] = k;
   __syncthreads();
-  const uint64_t mine = key[tid];
-  if (mine == ~0ull) return;
-  const uint32_t v = (uint32_t)(mine >> 32);
-  // first sorted position with this id (lower bound of v * 2^32)
-  int lo = 0, hi = tid;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((uint32_t)(key[mid] >> 32) < v) lo = mid + 1;
-    else hi = mid;
+  const uint64_t* sk = key[buf];
+  if (k != ~0ull) {
+    const uint32_t v = (uint32_t)(k >> 32);
+    // first sorted position with this id (lower bound of v * 2^32)
+    int lo = 0, hi = tid;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((uint32_t)(sk[mid] >> 32) < v) lo = mid + 1;
+      else hi = mid;
+    }
+    rank[c * kChunk + (int64_t)(uint32_t)k] = tid - lo;
+    if (tid + 1 == kChunk || (uint32_t)(sk[tid + 1] >> 32) != v) {
+      if (full_row) cnt[v] = tid - lo + 1;
+      else counts[c * vocab + v] = tid - lo + 1;
+    }
   }
-  rank[c * kChunk + (int64_t)(uint32_t)mine] = tid - lo;
-  if (tid + 1 == kChunk || (uint32_t)(key[tid + 1] >> 32) != v)
-    counts[c * vocab + v] = tid - lo + 1;
+  if (full_row) {
+    __syncthreads();
+    for (int v = tid; v < vocab; v += kChunk) counts[c * vocab + v] = cnt[v];
+  }
 }
 
 // counts [C][vocab] -> in place exclusive prefix over chunks; total[id].
@@ -85,12 +113,12 @@ __global__ void __launch_bounds__(256) row_offsets_kernel(int32_t* __restrict__ 
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= vocab) return;
   int32_t run = 0;
-  for (int64_t c0 = 0; c0 < C; c0 += 8) {
-    int32_t n[8];
+  for (int64_t c0 = 0; c0 < C; c0 += 32) {
+    int32_t n[32];  // unconditional loads: past the last chunk re-read it
 #pragma unroll
-    for (int u = 0; u < 8; ++u) n[u] = c0 + u < C ? counts[(c0 + u) * vocab + v] : 0;
+    for (int u = 0; u < 32; ++u) n[u] = counts[(c0 + u < C ? c0 + u : C - 1) * vocab + v];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 32; ++u)
       if (c0 + u < C) {
         counts[(c0 + u) * vocab + v] = run;
         run += n[u];
@@ -141,103 +169,127 @@ __global__ void __launch_bounds__(1024) id_scan_kernel(const int32_t* __restrict
   if (tid == 0) start[vocab] = carry;
 }
 
+// order[p] = t and info[p] = id | whole << 31 for sorted position p, where
+// whole says that the id's positions all lie in one segment.
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                       int64_t vocab,
                                                       const int32_t* __restrict__ rank,
                                                       const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ start,
-                                                      int32_t* __restrict__ order) {
+                                                      int32_t* __restrict__ order,
+                                                      uint32_t* __restrict__ info) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const int32_t v = ids[t];
   if (v < 0 || v >= vocab) return;
   const int64_t c = t / kChunk;
-  order[start[v] + counts[c * vocab + v] + rank[t]] = (int32_t)t;
+  const int32_t lo = start[v], hi = start[v + 1];
+  const int64_t pos = lo + counts[c * vocab + v] + rank[t];
+  order[pos] = (int32_t)t;
+  info[pos] = (uint32_t)v | ((lo / kSeg == (hi - 1) / kSeg) ? 0x80000000u : 0u);
 }
 
-// One workgroup per segment [kSeg s, kSeg s + kSeg) of the sorted order (n_valid
-// = start[vocab] positions in all).  Threads own 4 columns each; the rows of a
-// run are added in position order.  Partial runs go to part[s][0] (the run at
-// the segment's first position) and part[s][1] (the run at its last position,
-// when that is a different run).
-__global__ void __launch_bounds__(128) segment_kernel(const float* __restrict__ g, int64_t N,
-                                                      const int32_t* __restrict__ ids,
-                                                      const int32_t* __restrict__ start,
-                                                      int64_t vocab,
-                                                      const int32_t* __restrict__ order,
-                                                      float* __restrict__ GE,
-                                                      float* __restrict__ part) {
-  __shared__ int32_t s_tok[kSeg], s_id[kSeg];
-  const int64_t nvalid = start[vocab];
-  const int64_t p0 = (int64_t)blockIdx.x * kSeg;
-  if (p0 >= nvalid) return;
-  const int n = (int)min((int64_t)kSeg, nvalid - p0);
-  if (threadIdx.x < n) {
-    const int32_t t = order[p0 + threadIdx.x];
-    s_tok[threadIdx.x] = t;
-    s_id[threadIdx.x] = ids[t];
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// The partials of an id spanning segments s0..s1 summed in segment order: its
+// run is the last one of s0 (slot 1, unless it starts the segment: slot 0) and
+// the first one (slot 0) of every later segment.  kFinishBatch partials in
+// flight at a time.
+__device__ __forceinline__ void combine_partials(const float* __restrict__ part, int64_t N,
+                                                 int64_t c4, int64_t lo, int64_t hi,
+                                                 float* __restrict__ row) {
+  const int64_t s0 = lo / kSeg, s1 = (hi - 1) / kSeg;
+  float4 acc = reinterpret_cast<const float4*>(part + (s0 * 2 + (lo % kSeg == 0 ? 0 : 1)) * N)[c4];
+  for (int64_t sb = s0 + 1; sb <= s1; sb += kFinishBatch) {
+    float4 x[kFinishBatch];  // unconditional loads: past s1 re-read s1
+#pragma unroll
+    for (int u = 0; u < kFinishBatch; ++u)
+      x[u] = reinterpret_cast<const float4*>(part + (sb + u <= s1 ? sb + u : s1) * 2 * N)[c4];
+#pragma unroll
+    for (int u = 0; u < kFinishBatch; ++u)
+      if (sb + u <= s1) acc = add4(acc, x[u]);
   }
-  __syncthreads();
-  for (int64_t c4 = threadIdx.x; c4 < N / 4; c4 += blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int a = 0;  // first position of the current run
-    for (int pb = 0; pb < n; pb += 8) {
-      float4 x[8];  // eight rows in flight
+  reinterpret_cast<float4*>(row)[c4] = acc;
+}
+
+// One wave per (segment [kSeg s, kSeg s + kSeg) of the sorted order, block of
+// kSegCols float4 columns); n_valid = start[vocab] sorted positions in all.
+// Lane p < kSeg holds position p's token and info; each lane issues the loads
+// of all the segment's rows for its 4 columns at once, then adds the rows of
+// each run in position order.  A run that is its id's whole range is written
+// to G_E; otherwise it is a partial (at most the segment's first and last
+// run) and goes to part[s][0] (the run at the segment's first position) or
+// part[s][1] (the run at its last position).
+__global__ void __launch_bounds__(kSegCols) segment_kernel(const float* __restrict__ g, int64_t N,
+                                                           int64_t T,
+                                                           const int32_t* __restrict__ start,
+                                                           int64_t vocab,
+                                                           const int32_t* __restrict__ order,
+                                                           const uint32_t* __restrict__ info,
+                                                           float* __restrict__ GE,
+                                                           float* __restrict__ part) {
+  const int lane = threadIdx.x;
+  const int64_t seg = blockIdx.x, p0 = seg * kSeg;
+  int32_t my_t = 0;
+  uint32_t my_info = 0;
+  if (lane < kSeg && p0 + lane < T) {
+    my_t = order[p0 + lane];
+    my_info = info[p0 + lane];
+  }
+  const int64_t nvalid = start[vocab];
+  if (p0 >= nvalid) return;  // whole wave
+  const int n = (int)min((int64_t)kSeg, nvalid - p0);
+  const int64_t nc4 = N / 4;
+  const int64_t c4 = (int64_t)blockIdx.y * kSegCols + lane;
+  const bool col = c4 < nc4;
+  const int64_t cl = col ? c4 : nc4 - 1;  // lanes past the last column load a valid one
+  float4 x[kSeg];  // every row of the segment in flight (past n: the last row again)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        x[u] = pb + u < n ? reinterpret_cast<const float4*>(g + (int64_t)s_tok[pb + u] * N)[c4]
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int u = 0; u < kSeg; ++u) {
+    const int32_t t = __builtin_amdgcn_readlane(my_t, u < n ? u : n - 1);
+    x[u] = reinterpret_cast<const float4*>(g + (int64_t)t * N)[cl];
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int a = 0;  // first position of the current run
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int p = pb + u;
-        if (p >= n) break;
-        acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
-        const int v = s_id[p];
-        if (p + 1 == n || s_id[p + 1] != v) {  // run [a, p] ends
-          const int64_t lo = start[v], hi = start[v + 1];
-          float* dst;
-          if (lo >= p0 && hi <= p0 + n) dst = GE + (int64_t)v * N;                // whole id
-          else dst = part + ((int64_t)blockIdx.x * 2 + (a == 0 ? 0 : 1)) * N;     // partial
-          reinterpret_cast<float4*>(dst)[c4] = acc;
-          acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          a = p + 1;
+  for (int p = 0; p < kSeg; ++p) {
+    if (p < n) {
+      acc = add4(acc, x[p]);
+      const uint32_t inf = (uint32_t)__builtin_amdgcn_readlane((int)my_info, p);
+      const uint32_t v = inf & 0x7FFFFFFFu;
+      const uint32_t vn =
+          (uint32_t)__builtin_amdgcn_readlane((int)my_info, p + 1 < kSeg ? p + 1 : p) & 0x7FFFFFFFu;
+      if (p + 1 == n || vn != v) {  // run [a, p] ends
+        if (inf >> 31) {
+          if (col) reinterpret_cast<float4*>(GE + (int64_t)v * N)[c4] = acc;
+        } else {
+          const int slot = a == 0 ? 0 : 1;
+          if (col) reinterpret_cast<float4*>(part + (seg * 2 + slot) * N)[c4] = acc;
         }
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        a = p + 1;
       }
     }
   }
 }
 
-// Per id: rows of absent ids are zero; an id whose range spans segments s0..s1
-// sums its partials in segment order (its run is the last one of s0, slot 1
-// unless it starts the segment, and the first one of every later segment).
+// Per id: the zero row of an absent id, or the in-order sum of the partials of
+// an id whose range spans segments; ids written whole by segment_kernel return.
 __global__ void __launch_bounds__(128) finish_kernel(int64_t N, const int32_t* __restrict__ start,
                                                      int64_t vocab, const float* __restrict__ part,
                                                      float* __restrict__ GE) {
   for (int64_t v = blockIdx.x; v < vocab; v += gridDim.x) {
     const int64_t lo = start[v], hi = start[v + 1];
-    float4* row = reinterpret_cast<float4*>(GE + v * N);
     if (hi == lo) {
       for (int64_t c4 = threadIdx.x; c4 < N / 4; c4 += blockDim.x)
-        row[c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+        reinterpret_cast<float4*>(GE + v * N)[c4] = make_float4(0.f, 0.f, 0.f, 0.f);
       continue;
     }
-    const int64_t s0 = lo / kSeg, s1 = (hi - 1) / kSeg;
-    if (s0 == s1) continue;  // written whole by segment_kernel
-    for (int64_t c4 = threadIdx.x; c4 < N / 4; c4 += blockDim.x) {
-      float4 acc = reinterpret_cast<const float4*>(part + (s0 * 2 + (lo % kSeg == 0 ? 0 : 1)) * N)[c4];
-      for (int64_t sb = s0 + 1; sb <= s1; sb += 8) {
-        float4 x[8];  // eight partials in flight, added in segment order
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          x[u] = sb + u <= s1 ? reinterpret_cast<const float4*>(part + (sb + u) * 2 * N)[c4]
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
-        }
-      }
-      row[c4] = acc;
-    }
+    if (lo / kSeg == (hi - 1) / kSeg) continue;  // written whole by segment_kernel
+    for (int64_t c4 = threadIdx.x; c4 < N / 4; c4 += blockDim.x)
+      combine_partials(part, N, c4, lo, hi, GE + v * N);
   }
 }
 
@@ -248,15 +300,18 @@ __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
 
 static size_t a256(size_t v) { return (v + 255) / 256 * 256; }
 
+static int64_t seg_col_blocks(int64_t N) { return (N / 4 + kSegCols - 1) / kSegCols; }
+
 size_t embedding_workspace_bytes(int64_t T, int64_t N, int64_t vocab) {
   const int64_t C = (T + kChunk - 1) / kChunk, S = (T + kSeg - 1) / kSeg;
-  return a256((size_t)C * vocab * 4) + a256((size_t)T * 4) * 2 + a256((size_t)vocab * 4) +
+  return a256((size_t)C * vocab * 4) + a256((size_t)T * 4) * 3 + a256((size_t)vocab * 4) +
          a256((size_t)(vocab + 1) * 4) + a256((size_t)S * 2 * N * 4);
 }
 
 hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, int64_t N,
                                  int64_t vocab, float* GE, void* workspace, hipStream_t s) {
   const int64_t C = (T + kChunk - 1) / kChunk, S = (T + kSeg - 1) / kSeg;
+  const int64_t CB = seg_col_blocks(N);
   char* w = reinterpret_cast<char*>(workspace);
   int32_t* counts = reinterpret_cast<int32_t*>(w);
   w += a256((size_t)C * vocab * 4);
@@ -264,30 +319,36 @@ hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, 
   w += a256((size_t)T * 4);
   int32_t* order = reinterpret_cast<int32_t*>(w);
   w += a256((size_t)T * 4);
+  uint32_t* info = reinterpret_cast<uint32_t*>(w);
+  w += a256((size_t)T * 4);
   int32_t* total = reinterpret_cast<int32_t*>(w);
   w += a256((size_t)vocab * 4);
   int32_t* start = reinterpret_cast<int32_t*>(w);
   w += a256((size_t)(vocab + 1) * 4);
   float* part = reinterpret_cast<float*>(w);
 
-  const int64_t ncnt = C * vocab;
-  int64_t zb = (ncnt + 255) / 256;
-  if (zb > 4096) zb = 4096;
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((uint32_t)(zb > 0 ? zb : 1)), dim3(256), 0, s, counts,
-                     ncnt);
+  // small vocabularies: each rank workgroup writes its whole row of counts
+  const int full_row = vocab <= kRankRowMax;
+  if (!full_row) {
+    const int64_t ncnt = C * vocab;
+    int64_t zb = (ncnt + 255) / 256;
+    if (zb > 4096) zb = 4096;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((uint32_t)(zb > 0 ? zb : 1)), dim3(256), 0, s, counts,
+                       ncnt);
+  }
   if (T > 0)
     hipLaunchKernelGGL(rank_kernel, dim3((uint32_t)C), dim3(kChunk), 0, s, ids, T, vocab, rank,
-                       counts);
+                       counts, full_row);
   hipLaunchKernelGGL(row_offsets_kernel, dim3((uint32_t)((vocab + 255) / 256)), dim3(256), 0, s,
                      counts, C, vocab, total);
   hipLaunchKernelGGL(id_scan_kernel, dim3(1), dim3(1024), 0, s, total, vocab, start);
   if (T > 0) {
     hipLaunchKernelGGL(scatter_kernel, dim3((uint32_t)((T + 255) / 256)), dim3(256), 0, s, ids, T,
-                       vocab, rank, counts, start, order);
-    hipLaunchKernelGGL(segment_kernel, dim3((uint32_t)S), dim3(128), 0, s, g, N, ids, start, vocab,
-                       order, GE, part);
+                       vocab, rank, counts, start, order, info);
+    hipLaunchKernelGGL(segment_kernel, dim3((uint32_t)S, (uint32_t)CB), dim3(kSegCols), 0, s, g, N,
+                       T, start, vocab, order, info, GE, part);
   }
-  const int64_t fb = vocab < 2048 ? vocab : 2048;
+  const int64_t fb = vocab < 65536 ? vocab : 65536;
   hipLaunchKernelGGL(finish_kernel, dim3((uint32_t)fb), dim3(128), 0, s, N, start, vocab, part, GE);
   return hipGetLastError();
 }

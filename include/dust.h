@@ -226,7 +226,7 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
  *   ids device [T] int32; g_hat device [T,N] fp32 (N % 4 == 0);
  *   G_E device [vocab,N] fp32 out;
  *   workspace >= dust_embedding_workspace_size(T, N, vocab) bytes (about
- *   T/512 * vocab * 4 + T/32 * N * 8 + 8 T + 8 vocab).
+ *   T/512 * vocab * 4 + T/32 * N * 8 + 12 T + 8 vocab).
  * Requires T <= 2^22, N <= 2^20, vocab <= 2^24 and ceil(T/512) * vocab <= 2^31
  * (DUST_ERR_UNSUPPORTED otherwise). */
 dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t T, int64_t N,

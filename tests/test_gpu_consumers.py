@@ -16,9 +16,12 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("T,N,vocab,layout", [(3000, 100, 257, "zipf"), (1, 4, 3, "zipf"),
                                               (2048, 8, 1, "zipf"), (16384, 512, 4096, "zipf"),
                                               (640, 12, 10, "blocks64"), (700, 8, 10, "blocks70"),
-                                              (300, 4, 5, "invalid")])
+                                              (300, 4, 5, "invalid"),
+                                              # vocabulary above the in-pass clear of the
+                                              # counts; more chunks than one batch of 32
+                                              (3000, 8, 20000, "zipf"), (20000, 16, 300, "zipf")])
 def test_embedding_grad(T, N, vocab, layout):
-    """Zipf ids (a few ids own long runs that span many 64-position segments of
+    """Zipf ids (a few ids own long runs that span many 32-position segments of
     the sorted order), ids whose runs fill segments exactly or straddle them,
     and inputs whose ids are all out of range."""
     dust = need_gpu()
