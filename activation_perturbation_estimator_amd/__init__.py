@@ -55,6 +55,28 @@ def _dev(t, name: str):
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape=None, dtypes=None, device=None) -> None:
+    """Shape, dtype and device of a tensor the library reads or writes: the C
+    ABI takes bare pointers, so a wrong-sized buffer must be refused here."""
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtypes is not None:
+        dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _f32():
+    return _torch().float32
+
+
+def _fp():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
 def _stream(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -75,10 +97,26 @@ def _events(stage_events) -> Optional[object]:
 def _workspace(nbytes: int, device, workspace):
     torch = _torch()
     if workspace is not None:
+        _expect(workspace, "workspace", device=device)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return workspace
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _outputs(out, shapes, device, names):
+    """Preallocated outputs (float32, exact shapes, on `device`), or fresh ones."""
+    torch = _torch()
+    if out is None:
+        return tuple(torch.empty(sh, dtype=torch.float32, device=device) for sh in shapes)
+    out = (out,) if len(shapes) == 1 and not isinstance(out, (tuple, list)) else tuple(out)
+    if len(out) != len(shapes):
+        raise ValueError(f"out must hold {len(shapes)} tensors")
+    for o, sh, nm in zip(out, shapes, names):
+        _expect(o, nm, sh, _f32(), device)
+    return out
 
 
 def version() -> str:
@@ -107,18 +145,15 @@ def head_estimate(logits, targets, X, *, sigma: float, K: int, gamma: float = 0.
     GPU.  Returns (g_hat [T,V] f32, G_W [V,d] f32) and, with return_losses,
     the per-draw losses [K,T].  ``out`` may pass preallocated (g_hat, G_W)."""
     torch = _torch()
-    lib = _lib.load()
     T, V = logits.shape
     d = X.shape[1]
-    if X.shape[0] != T or targets.shape != (T,) or targets.dtype != torch.int32:
-        raise ValueError("shape/dtype mismatch: logits [T,V], targets [T] int32, X [T,d]")
-    L = T if seq_len is None else int(seq_len)
     dev = logits.device
-    if out is None:
-        g = torch.empty((T, V), dtype=torch.float32, device=dev)
-        G = torch.empty((V, d), dtype=torch.float32, device=dev)
-    else:
-        g, G = out
+    _expect(logits, "logits", dtypes=_fp())
+    _expect(targets, "targets", (T,), torch.int32, dev)
+    _expect(X, "X", (T, d), _fp(), dev)
+    L = T if seq_len is None else int(seq_len)
+    g, G = _outputs(out, [(T, V), (V, d)], dev, ["g_hat", "G_W"])
+    lib = _lib.load()
     losses = torch.empty((K, T), dtype=torch.float32, device=dev) if return_losses else None
     nbytes = lib.dust_head_workspace_size(T, V, d, K, gamma)
     ws = _workspace(nbytes, dev, workspace)
@@ -137,19 +172,14 @@ def linear_estimate(X, c, *, N: int, sigma: float, gamma: float = 0.0, seed: int
     """Hidden linear layer: X [T,d_in] (f32/bf16), caller-centred loss decreases
     c [K,T] f32 measured with dust noise (seed, stream, draws 0..K-1) of width N.
     Returns (g_hat [T,N] f32, G_W [N,d_in] f32)."""
-    torch = _torch()
-    lib = _lib.load()
     T, d_in = X.shape
     K = c.shape[0]
-    if c.shape != (K, T) or c.dtype != torch.float32:
-        raise ValueError("c must be float32 [K,T]")
-    L = T if seq_len is None else int(seq_len)
     dev = X.device
-    if out is None:
-        g = torch.empty((T, N), dtype=torch.float32, device=dev)
-        G = torch.empty((N, d_in), dtype=torch.float32, device=dev)
-    else:
-        g, G = out
+    _expect(X, "X", dtypes=_fp())
+    _expect(c, "c", (K, T), _f32(), dev)
+    L = T if seq_len is None else int(seq_len)
+    g, G = _outputs(out, [(T, N), (N, d_in)], dev, ["g_hat", "G_W"])
+    lib = _lib.load()
     nbytes = lib.dust_linear_workspace_size(T, d_in, N, K, gamma)
     ws = _workspace(nbytes, dev, workspace)
     st = lib.dust_linear_estimate(
@@ -174,8 +204,8 @@ def noise(*, seed: int, stream: int = 0, draw0: int = 0, ndraw: int, T: int, N: 
 def philox4x32_10(seed: int, ctr):
     """Raw Philox4x32-10 blocks for counters ctr (int32/uint32 tensor [n,4] on GPU)."""
     torch = _torch()
-    if ctr.dim() != 2 or ctr.shape[1] != 4 or ctr.element_size() != 4:
-        raise ValueError("ctr must be a 32-bit [n,4] tensor")
+    if ctr.dim() != 2 or ctr.shape[1] != 4 or ctr.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("ctr must be an int32 or uint32 [n,4] tensor")
     out = torch.empty_like(ctr)
     st = _lib.load().dust_philox4x32_10(int(seed), _dev(ctr, "ctr"), out.data_ptr(),
                                         ctr.shape[0], _stream(ctr.device))
@@ -187,6 +217,8 @@ def head_losses(logits, targets, *, sigma: float, K: int, seed: int = 1, stream:
     """Per-draw perturbed LM-head losses [K,T] f32."""
     torch = _torch()
     T, V = logits.shape
+    _expect(logits, "logits", dtypes=_fp())
+    _expect(targets, "targets", (T,), torch.int32, logits.device)
     out = torch.empty((K, T), dtype=torch.float32, device=logits.device)
     st = _lib.load().dust_head_losses(_dev(logits, "logits"), _dtype_code(logits),
                                       _dev(targets, "targets"), T, V, float(sigma), int(K),
@@ -198,9 +230,9 @@ def head_losses(logits, targets, *, sigma: float, K: int, seed: int = 1, stream:
 
 def centre(x, out=None):
     """c[i,t] = mean_j x[j,t] - x[i,t] for per-draw losses x [K,T] f32."""
-    torch = _torch()
     K, T = x.shape
-    c = torch.empty_like(x) if out is None else out
+    _expect(x, "x", dtypes=_f32())
+    (c,) = _outputs(out, [(K, T)], x.device, ["out"])
     st = _lib.load().dust_centre(_dev(x, "x"), K, T, _dev(c, "c"), _stream(x.device))
     _lib.check("dust_centre", st)
     return c
@@ -208,9 +240,9 @@ def centre(x, out=None):
 
 def reward_scan(c, *, seq_len: int, gamma: float, out=None):
     """r = segmented reverse gamma-scan of c [K,T] f32."""
-    torch = _torch()
     K, T = c.shape
-    r = torch.empty_like(c) if out is None else out
+    _expect(c, "c", dtypes=_f32())
+    (r,) = _outputs(out, [(K, T)], c.device, ["out"])
     st = _lib.load().dust_reward_scan(_dev(c, "c"), K, T, int(seq_len), float(gamma),
                                       _dev(r, "r"), _stream(c.device))
     _lib.check("dust_reward_scan", st)
@@ -219,9 +251,9 @@ def reward_scan(c, *, seq_len: int, gamma: float, out=None):
 
 def error_estimate(r, *, N: int, sigma: float, seed: int = 1, stream: int = 0, out=None):
     """g_hat[t,n] = -(1/(K sigma)) sum_i r[i,t] a^(i)_t[n] with regenerated noise."""
-    torch = _torch()
     K, T = r.shape
-    g = torch.empty((T, N), dtype=torch.float32, device=r.device) if out is None else out
+    _expect(r, "r", dtypes=_f32())
+    (g,) = _outputs(out, [(T, int(N))], r.device, ["out"])
     st = _lib.load().dust_error_estimate(_dev(r, "r"), K, T, int(N), float(sigma), int(seed),
                                          int(stream), _dev(g, "g_hat"), _stream(r.device))
     _lib.check("dust_error_estimate", st)
@@ -230,11 +262,12 @@ def error_estimate(r, *, N: int, sigma: float, seed: int = 1, stream: int = 0, o
 
 def outer_sum(g_hat, X, out=None, workspace=None):
     """G_W = g_hat^T X (sum over tokens), fp32 [N,d]."""
-    torch = _torch()
-    lib = _lib.load()
     T, N = g_hat.shape
     d = X.shape[1]
-    G = torch.empty((N, d), dtype=torch.float32, device=g_hat.device) if out is None else out
+    _expect(g_hat, "g_hat", dtypes=_f32())
+    _expect(X, "X", (T, d), _fp(), g_hat.device)
+    (G,) = _outputs(out, [(N, d)], g_hat.device, ["out"])
+    lib = _lib.load()
     nbytes = lib.dust_outer_sum_workspace_size(T, N, d)
     ws = _workspace(nbytes, g_hat.device, workspace)
     st = lib.dust_outer_sum(_dev(g_hat, "g_hat"), _dev(X, "X"), _dtype_code(X), T, N, d,
@@ -248,12 +281,11 @@ def perturbed_linear(X, W, *, sigma: float, seed: int = 1, stream: int = 0, draw
                      ndraw: int = 1, out=None):
     """Y[k] = X W^T + sigma a^(draw0+k) as float32 [ndraw, T, N]: the caller's
     perturbed forward, with the noise dust_linear_estimate regenerates."""
-    torch = _torch()
     T, d = X.shape
     N = W.shape[0]
-    if W.shape[1] != d or W.dtype != X.dtype:
-        raise ValueError("X [T,d] and W [N,d] must share d and dtype")
-    Y = torch.empty((ndraw, T, N), dtype=torch.float32, device=X.device) if out is None else out
+    _expect(X, "X", dtypes=_fp())
+    _expect(W, "W", (N, d), X.dtype, X.device)
+    (Y,) = _outputs(out, [(int(ndraw), T, N)], X.device, ["out"])
     st = _lib.load().dust_perturbed_linear(_dev(X, "X"), _dev(W, "W"), _dtype_code(X), T, d, N,
                                            float(sigma), int(seed), int(stream), int(draw0),
                                            int(ndraw), _dev(Y, "Y"), _stream(X.device))
@@ -265,11 +297,11 @@ def embedding_grad(ids, g_hat, vocab: int, out=None, workspace=None):
     """G_E[v] = sum_{t: ids[t] = v} g_hat[t] as float32 [vocab, N] (one-hot input:
     the outer product is a scatter-add; deterministic order)."""
     torch = _torch()
-    lib = _lib.load()
     T, N = g_hat.shape
-    if ids.shape != (T,) or ids.dtype != torch.int32:
-        raise ValueError("ids must be int32 [T]")
-    G = torch.empty((vocab, N), dtype=torch.float32, device=g_hat.device) if out is None else out
+    _expect(g_hat, "g_hat", dtypes=_f32())
+    _expect(ids, "ids", (T,), torch.int32, g_hat.device)
+    (G,) = _outputs(out, [(int(vocab), N)], g_hat.device, ["out"])
+    lib = _lib.load()
     ws = _workspace(lib.dust_embedding_workspace_size(T, N, int(vocab)), g_hat.device, workspace)
     st = lib.dust_embedding_grad(_dev(ids, "ids"), _dev(g_hat, "g_hat"), T, N, int(vocab),
                                  _dev(G, "G_E"), ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -280,6 +312,8 @@ def embedding_grad(ids, g_hat, vocab: int, out=None, workspace=None):
 
 def sgd_momentum_(W, G, m, *, lr: float, momentum: float = 0.9, weight_decay: float = 0.0):
     """In place: m = momentum m + (G + wd W); W -= lr m (float32 tensors of one size)."""
+    for t, nm in ((W, "W"), (G, "G"), (m, "m")):
+        _expect(t, nm, W.shape, _f32(), W.device)
     st = _lib.load().dust_sgd_momentum(_dev(W, "W"), _dev(G, "G"), _dev(m, "m"), W.numel(),
                                        float(lr), float(momentum), float(weight_decay),
                                        _stream(W.device))
@@ -290,6 +324,8 @@ def sgd_momentum_(W, G, m, *, lr: float, momentum: float = 0.9, weight_decay: fl
 def adam_(W, G, m, v, *, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
           eps: float = 1e-8, weight_decay: float = 0.0):
     """In place Adam step (bias-corrected, PyTorch semantics) on float32 tensors."""
+    for t, nm in ((W, "W"), (G, "G"), (m, "m"), (v, "v")):
+        _expect(t, nm, W.shape, _f32(), W.device)
     st = _lib.load().dust_adam(_dev(W, "W"), _dev(G, "G"), _dev(m, "m"), _dev(v, "v"), W.numel(),
                                float(lr), float(beta1), float(beta2), float(eps),
                                float(weight_decay), int(step), _stream(W.device))
@@ -301,7 +337,9 @@ def ce_grad(logits, targets, out=None):
     """softmax(z) - onehot(y) as float32 [T,V]: the closed-form LM-head gradient."""
     torch = _torch()
     T, V = logits.shape
-    o = torch.empty((T, V), dtype=torch.float32, device=logits.device) if out is None else out
+    _expect(logits, "logits", dtypes=_fp())
+    _expect(targets, "targets", (T,), torch.int32, logits.device)
+    (o,) = _outputs(out, [(T, V)], logits.device, ["out"])
     st = _lib.load().dust_ce_grad(_dev(logits, "logits"), _dtype_code(logits),
                                   _dev(targets, "targets"), T, V, _dev(o, "out"),
                                   _stream(logits.device))
@@ -312,6 +350,7 @@ def ce_grad(logits, targets, out=None):
 def check_targets(targets, V: int) -> bool:
     """True when 0 <= targets < V everywhere (waits for the device)."""
     torch = _torch()
+    _expect(targets, "targets", dtypes=torch.int32)
     flag = torch.empty(1, dtype=torch.int32, device=targets.device)
     st = _lib.load().dust_check_targets(_dev(targets, "targets"), targets.numel(), int(V),
                                         flag.data_ptr(), _stream(targets.device))
