@@ -39,7 +39,7 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
     for (int b = 0; b < kNB; ++b) {
       const uint32_t j = (uint32_t)(b * 64 * kW + wave * 64 + lane);
       float a0, a1, a2, a3;
-      normal4(j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
+      normal4_scaled(j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
       acc[4 * b] = fmaf(ri, a0, acc[4 * b]);
       acc[4 * b + 1] = fmaf(ri, a1, acc[4 * b + 1]);
       acc[4 * b + 2] = fmaf(ri, a2, acc[4 * b + 2]);
@@ -68,7 +68,8 @@ static hipError_t launch_ee_t(const float* r, int64_t K, int64_t T, int64_t N, f
 hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
                                  uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const float scale = -1.0f / ((float)K * sigma);
+  // the noise comes divided by kBoxMullerScale (normal4_scaled)
+  const float scale = -kBoxMullerScale / ((float)K * sigma);
   const HeadShape h = wide_shape(N);
 #define DUST_EE_CASE(NB, W) \
   if (h.nb == NB && h.w == W) return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, g_hat, s);

@@ -109,6 +109,27 @@ __device__ __forceinline__ void normal4(uint32_t j, uint32_t token, uint32_t dra
   box_muller4(philox10_row(token, j, draw, stream, k0, k1), a0, a1, a2, a3);
 }
 
+// The same normals divided by sqrt(2 ln 2): the radius sqrt(-2 ln u) is
+// sqrt(2 ln 2) sqrt(-log2 u), and sqrt(-log2 u) is one v_sqrt with a negated
+// operand, one multiply fewer per pair.  Kernels that only ever scale the noise
+// (sigma a in a perturbation, r a in the error estimate) use these and fold
+// kBoxMullerScale into their scalar factor.
+constexpr float kBoxMullerScale = 1.17741002251547469101f;  // sqrt(2 ln 2)
+
+__device__ __forceinline__ void normal4_scaled(uint32_t j, uint32_t token, uint32_t draw,
+                                               uint32_t stream, uint32_t k0, uint32_t k1,
+                                               float& a0, float& a1, float& a2, float& a3) {
+  const u32x4 x = philox10_row(token, j, draw, stream, k0, k1);
+  const float u0 = unit_open(x.x), u1 = unit_open(x.y);
+  const float u2 = unit_open(x.z), u3 = unit_open(x.w);
+  const float r0 = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u0));
+  const float r1 = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u2));
+  a0 = r0 * __builtin_amdgcn_cosf(u1);
+  a1 = r0 * __builtin_amdgcn_sinf(u1);
+  a2 = r1 * __builtin_amdgcn_cosf(u3);
+  a3 = r1 * __builtin_amdgcn_sinf(u3);
+}
+
 // ---------------------------------------------------------------------------
 // Wavefront (64-lane) reductions.  DPP steps inside rows of 16 lanes, then the
 // four row sums combined in a fixed order, so the result is deterministic and
@@ -120,16 +141,17 @@ __device__ __forceinline__ float dpp_f(float v) {
       __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
 }
 
+// Row sums R0..R3 in every lane of their row, then row_bcast:15 adds R0 into
+// row 1 and R2 into row 3, and row_bcast:31 adds row 1's R0 + R1 into row 3:
+// lane 63 holds (R2 + R3) + (R0 + R1).
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
   v += dpp_f<0x140>(v);  // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -180,6 +180,7 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
   // of the half (one token, 4 columns: one Philox block) and writes every draw
   // of an item before moving on, so only one item's product is live.
   constexpr int kYRow = kFN + 4;
+  const float sigma_s = sigma * kBoxMullerScale;  // the noise comes divided by it
   float* tile = reinterpret_cast<float*>(flds);
   const int64_t nblk = N >> 2;
 #pragma unroll
@@ -207,12 +208,13 @@ perturbed_linear_kernel(const void* __restrict__ Xv, const void* __restrict__ Wv
 #pragma unroll 2
         for (int64_t k = 0; k < ndraw; ++k) {
           float a0, a1, a2, a3;
-          normal4((uint32_t)j, (uint32_t)t, draw0 + (uint32_t)k, stream, k0, k1, a0, a1, a2, a3);
+          normal4_scaled((uint32_t)j, (uint32_t)t, draw0 + (uint32_t)k, stream, k0, k1, a0, a1,
+                         a2, a3);
           ff32x4_t o;
-          o.x = fmaf(sigma, a0, base.x);
-          o.y = fmaf(sigma, a1, base.y);
-          o.z = fmaf(sigma, a2, base.z);
-          o.w = fmaf(sigma, a3, base.w);
+          o.x = fmaf(sigma_s, a0, base.x);
+          o.y = fmaf(sigma_s, a1, base.y);
+          o.z = fmaf(sigma_s, a2, base.z);
+          o.w = fmaf(sigma_s, a3, base.w);
           // streaming store: Y is written once and is far larger than the caches
           __builtin_nontemporal_store(o, reinterpret_cast<ff32x4_t*>(yt + k * T * N));
         }

@@ -178,7 +178,10 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
   const float ell0 = kLn2 * (__builtin_amdgcn_logf(S0) - zty);
   if constexpr (kZInLds) __syncthreads();
 
-  const float sl2e = sigma * kLog2e;
+  // The noise arrives divided by kBoxMullerScale (normal4_scaled): every use
+  // scales it, so the constant rides on the scalar factors below and on g_t.
+  const float sl2e = sigma * kLog2e * kBoxMullerScale;
+  const float sigma_s = sigma * kBoxMullerScale;
   float acc_a[kFused ? kCols : 1];
   float acc_da[kFused ? kCols : 1];
   if constexpr (kFused) {
@@ -196,8 +199,8 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const int j = b * 64 * kW + wave * 64 + lane;
-      normal4((uint32_t)j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a[4 * b], a[4 * b + 1],
-              a[4 * b + 2], a[4 * b + 3]);
+      normal4_scaled((uint32_t)j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a[4 * b],
+                     a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]);
       float z0, z1, z2, z3;
       if constexpr (kZInLds) {
         const float4 zz = *reinterpret_cast<const float4*>(zs + 4 * j);
@@ -221,8 +224,8 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
   auto refresh_target_noise = [&](int64_t i) {
     if ((i & 63) == 0) {
       float a0, a1, a2, a3;
-      normal4((uint32_t)(y >> 2), (uint32_t)t, (uint32_t)(i + lane), stream, k0, k1, a0, a1, a2,
-              a3);
+      normal4_scaled((uint32_t)(y >> 2), (uint32_t)t, (uint32_t)(i + lane), stream, k0, k1, a0,
+                     a1, a2, a3);
       const int q = y & 3;
       ay_vec = q == 0 ? a0 : (q == 1 ? a1 : (q == 2 ? a2 : a3));
     }
@@ -230,7 +233,7 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
   // Loss change of draw i from its full sum S_i; accumulate or write it.
   auto finish = [&](int64_t i, float Si, const float* a) {
     const float ay = lane_value(ay_vec, (int)(i & 63));
-    const float delta = kLn2 * __builtin_amdgcn_logf(Si * inv_S0) - sigma * ay;
+    const float delta = kLn2 * __builtin_amdgcn_logf(Si * inv_S0) - sigma_s * ay;
     if constexpr (kFused) {
       sum_delta += delta;
 #pragma unroll
@@ -267,7 +270,7 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
 
   if constexpr (kFused) {
     const float dbar = sum_delta / (float)K;
-    const float scale = 1.0f / ((float)K * sigma);
+    const float scale = kBoxMullerScale / ((float)K * sigma);
     float* grow = g_hat + t * V;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {

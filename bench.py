@@ -44,10 +44,11 @@ HBM_BYTES_PER_S = 8.0e12
 #   Philox4x32-10 per block of 4 normals, counter (token, column/4, draw,
 #     stream): 16 lane-varying 32x32->64 products (2) + 18 xors (1) = 50 -> 12.5
 #   uniform map: alignbit + subtract = 3
-#   Box-Muller per pair: log, sqrt, cos, sin (4 each) + 3 multiplies = 19 -> 9.5
+#   Box-Muller per pair: log, sqrt, cos, sin (4 each) + 2 multiplies (radius times
+#     cosine and sine; the constant sqrt(2 ln 2) of the radius rides on sigma) = 18 -> 9
 #   perturbed cross-entropy: FMA + exp2 + add = 6
 #   accumulation of sum a and sum delta a: 2
-SLOTS = {"philox": (16 * 2 + 18) / 4, "uniform": 3, "box_muller": (4 * 4 + 3) / 2,
+SLOTS = {"philox": (16 * 2 + 18) / 4, "uniform": 3, "box_muller": (4 * 4 + 2) / 2,
          "cross_entropy": 6, "accumulate": 2}
 SLOTS_PER_NORMAL = sum(SLOTS.values())
 
