@@ -39,7 +39,7 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
     for (int b = 0; b < kNB; ++b) {
       const uint32_t j = (uint32_t)(b * 64 * kW + wave * 64 + lane);
       float a0, a1, a2, a3;
-      normal4_scaled(j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
+      normal4_scaled<true>(j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
       acc[4 * b] = fmaf(ri, a0, acc[4 * b]);
       acc[4 * b + 1] = fmaf(ri, a1, acc[4 * b + 1]);
       acc[4 * b + 2] = fmaf(ri, a2, acc[4 * b + 2]);

@@ -30,16 +30,30 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
 
 // One Philox4x32 round: counter words 0 and 2 are multiplied by the two
 // multipliers (full 64-bit products); the high halves are xor-ed with the other
-// two counter words and the round key; the low halves are kept.
-template <bool kBitop3>
+// two counter words and the round key; the low halves are kept.  The modes only
+// change how the xors are written for the compiler:
+//   kXorPlain : two-input xors, so that lane-uniform operands can be combined
+//               on the scalar unit first;
+//   kXorBitop3: one v_bitop3 per three-input xor (every operand lane-varying
+//               but the key);
+//   kXorC3Uniform: as kXorBitop3 for the new word 0, but c3 ^ k1 grouped for
+//               the new word 2, when c3 is lane-uniform (a vector instruction
+//               can take only one scalar operand, so a bitop3 there would need
+//               a copy of c3 into a vector register).
+enum PhiloxXor { kXorPlain, kXorBitop3, kXorC3Uniform };
+
+template <PhiloxXor kMode>
 __device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                              uint32_t& c3, uint32_t k0, uint32_t k1) {
   const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
   const uint64_t p1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
   uint32_t n0, n2;
-  if constexpr (kBitop3) {
+  if constexpr (kMode == kXorBitop3) {
     n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
     n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+  } else if constexpr (kMode == kXorC3Uniform) {
+    n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+    n2 = (uint32_t)(p0 >> 32) ^ (c3 ^ k1);
   } else {
     n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
     n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
@@ -56,25 +70,33 @@ __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2,
                                           uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r)
-    philox_round<true>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+    philox_round<kXorBitop3>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0,
+                             k1 + (uint32_t)r * kPhiloxW1);
   return u32x4{c0, c1, c2, c3};
 }
 
 // The same function for the counters of a noise row, (token, column/4, draw,
-// stream), where only the column word differs between lanes.  The column enters
-// through a xor, so the first rounds are mostly lane-uniform: their uniform
-// parts run on the scalar unit (plain xors let the compiler split them off),
-// and the vector work is 16 products instead of 20.  From the fourth round on
-// every word differs between lanes and each three-input xor is one bitop3.
+// stream).  With kColumnOnly, only the column word differs between lanes (one
+// token and draw per wave): the column enters through a xor, so the first
+// rounds are mostly lane-uniform; their uniform parts run on the scalar unit
+// (plain xors let the compiler split them off), the vector work is 16 products
+// instead of 20, and in the fourth round the fourth word is still uniform.
+// From the fifth round on every word differs between lanes and each
+// three-input xor is one bitop3.
+template <bool kColumnOnly>
 __device__ __forceinline__ u32x4 philox10_row(uint32_t token, uint32_t j, uint32_t draw,
                                               uint32_t stream, uint32_t k0, uint32_t k1) {
   uint32_t c0 = token, c1 = j, c2 = draw, c3 = stream;
 #pragma unroll
   for (int r = 0; r < 3; ++r)
-    philox_round<false>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+    philox_round<kXorPlain>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0,
+                            k1 + (uint32_t)r * kPhiloxW1);
+  philox_round<kColumnOnly ? kXorC3Uniform : kXorBitop3>(c0, c1, c2, c3, k0 + 3u * kPhiloxW0,
+                                                         k1 + 3u * kPhiloxW1);
 #pragma unroll
-  for (int r = 3; r < 10; ++r)
-    philox_round<true>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0, k1 + (uint32_t)r * kPhiloxW1);
+  for (int r = 4; r < 10; ++r)
+    philox_round<kXorBitop3>(c0, c1, c2, c3, k0 + (uint32_t)r * kPhiloxW0,
+                             k1 + (uint32_t)r * kPhiloxW1);
   return u32x4{c0, c1, c2, c3};
 }
 
@@ -106,7 +128,7 @@ __device__ __forceinline__ void box_muller4(const u32x4& x, float& a0, float& a1
 __device__ __forceinline__ void normal4(uint32_t j, uint32_t token, uint32_t draw,
                                         uint32_t stream, uint32_t k0, uint32_t k1,
                                         float& a0, float& a1, float& a2, float& a3) {
-  box_muller4(philox10_row(token, j, draw, stream, k0, k1), a0, a1, a2, a3);
+  box_muller4(philox10_row<false>(token, j, draw, stream, k0, k1), a0, a1, a2, a3);
 }
 
 // The same normals divided by sqrt(2 ln 2): the radius sqrt(-2 ln u) is
@@ -116,10 +138,12 @@ __device__ __forceinline__ void normal4(uint32_t j, uint32_t token, uint32_t dra
 // kBoxMullerScale into their scalar factor.
 constexpr float kBoxMullerScale = 1.17741002251547469101f;  // sqrt(2 ln 2)
 
+// kColumnOnly: the caller's token and draw are the same in every lane.
+template <bool kColumnOnly = false>
 __device__ __forceinline__ void normal4_scaled(uint32_t j, uint32_t token, uint32_t draw,
                                                uint32_t stream, uint32_t k0, uint32_t k1,
                                                float& a0, float& a1, float& a2, float& a3) {
-  const u32x4 x = philox10_row(token, j, draw, stream, k0, k1);
+  const u32x4 x = philox10_row<kColumnOnly>(token, j, draw, stream, k0, k1);
   const float u0 = unit_open(x.x), u1 = unit_open(x.y);
   const float u2 = unit_open(x.z), u3 = unit_open(x.w);
   const float r0 = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u0));

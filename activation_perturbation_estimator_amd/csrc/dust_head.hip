@@ -104,9 +104,9 @@ __device__ __forceinline__ void group_sum_n(float* v, float* red, int slot) {
     __syncthreads();
 #pragma unroll
     for (int d = 0; d < kN; ++d) {
-      float s = 0.f;
+      float s = red[(slot * kStride + d) * W];
 #pragma unroll
-      for (int q = 0; q < W; ++q) s += red[(slot * kStride + d) * W + q];
+      for (int q = 1; q < W; ++q) s += red[(slot * kStride + d) * W + q];
       v[d] = s;
     }
   }
@@ -195,12 +195,12 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
   // Noise of draw i for this lane's columns, and the lane's share of
   // S_i = sum_v 2^(ztilde_v + sigma log2(e) a_v).
   auto draw_noise = [&](int64_t i, float* a) -> float {
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    float p0, p1, p2, p3;  // set by the first block (no add to a zero start)
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const int j = b * 64 * kW + wave * 64 + lane;
-      normal4_scaled((uint32_t)j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a[4 * b],
-                     a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]);
+      normal4_scaled<true>((uint32_t)j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a[4 * b],
+                           a[4 * b + 1], a[4 * b + 2], a[4 * b + 3]);
       float z0, z1, z2, z3;
       if constexpr (kZInLds) {
         const float4 zz = *reinterpret_cast<const float4*>(zs + 4 * j);
@@ -214,10 +214,15 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
           z0 = z1 = z2 = z3 = -INFINITY;
         }
       }
-      p0 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b], z0));
-      p1 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 1], z1));
-      p2 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 2], z2));
-      p3 += __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 3], z3));
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b], z0));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 1], z1));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 2], z2));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(sl2e, a[4 * b + 3], z3));
+      if (b == 0) {
+        p0 = e0; p1 = e1; p2 = e2; p3 = e3;
+      } else {
+        p0 += e0; p1 += e1; p2 += e2; p3 += e3;
+      }
     }
     return (p0 + p1) + (p2 + p3);
   };
