@@ -421,9 +421,9 @@ ROWS = {"forward": run_forward, "embedding": run_embedding, "optim": run_optim,
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part "
-                                   "of it (the estimator shards by sequence, see the design "
-                                   "notes)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "bench.py measures one GPU; libdust has no multi-GPU path "
+                                   "(the estimator would shard by sequence, with one sum "
+                                   "all-reduce of G_W)", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import activation_perturbation_estimator_amd as dust

@@ -64,7 +64,7 @@ typedef enum {
     DUST_ERR_INVALID_ARG = 1, /* null pointer, bad size or parameter            */
     DUST_ERR_WORKSPACE = 2,   /* workspace pointer null or smaller than needed    */
     DUST_ERR_HIP = 3,         /* a HIP launch or runtime call failed              */
-    DUST_ERR_UNSUPPORTED = 4, /* valid request this build cannot serve (size)     */
+    DUST_ERR_UNSUPPORTED = 4, /* valid request beyond the library's size limits   */
     DUST_ERR_TARGETS = 5      /* dust_check_targets found a target out of range   */
 } dust_status;
 
