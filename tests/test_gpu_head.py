@@ -139,3 +139,19 @@ def test_mixed_input_dtypes(zbf16, xbf16):
 def test_extreme_seed_and_stream(seed, stream):
     z, y, X = synth.head_inputs(40, 300, 12, seed=14)
     _check(z, y, X, sigma=0.05, K=5, gamma=0.0, seed=seed, seq_len=40, stream=stream)
+
+
+def test_widest_vocabulary_with_discount():
+    # V = DUST_N_MAX: the unfused path with logits re-read from memory every draw,
+    # bf16 logits, and a discounted reward across a ragged sequence length
+    z, y, X = synth.head_inputs(6, 65536, 8, seed=21, bf16=True, zipf=True, logit_var=2.0,
+                                target_boost=3.0)
+    _check(z, y, X, sigma=0.02, K=4, gamma=0.7, seed=5, seq_len=3)
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.8])
+def test_largest_sigma(gamma):
+    # sigma = DUST_SIGMA_MAX: the perturbed exponents span the widest range the
+    # kernels accept (|sigma a| up to 8 x 5.77 nats above the clean maximum)
+    z, y, X = synth.head_inputs(64, 1000, 24, seed=22, bf16=False)
+    _check(z, y, X, sigma=8.0, K=16, gamma=gamma, seed=2, seq_len=16)
