@@ -89,7 +89,8 @@ def test_reward_scan_in_place_and_isolation():
 
 @pytest.mark.parametrize("K,T,N,L,gamma", [(16, 256, 512, 128, 0.0), (9, 60, 100, 20, 0.7),
                                            (70, 12, 4096, 12, 0.0), (5, 6, 8192, 3, 0.9),
-                                           (3, 4, 40000, 4, 0.0), (2, 3, 4, 1, 0.0)])
+                                           (3, 4, 40000, 4, 0.0), (2, 3, 4, 1, 0.0),
+                                           (3, 2, 65536, 2, 0.5)])  # N = DUST_N_MAX: 16 waves
 def test_error_estimate(K, T, N, L, gamma):
     dust = need_gpu()
     import torch
