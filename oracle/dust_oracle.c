@@ -20,7 +20,7 @@
  *   [P3] linlog.top explainer, section "the core of Dust: virtual population"
  *        -- a ~ N(0, I) per token; LM head: perturb cached logits, recompute CE.
  *
- * Readings taken where the pages are silent (each listed in the design notes):
+ * Readings taken where the pages are silent:
  *   - "centred" = subtract the per-token mean over the K draws.
  *   - noise stream = Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit
  *     seed, counter (token, column/4, draw, stream), mapped to uniforms in
