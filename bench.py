@@ -369,8 +369,9 @@ def run_optim(args, torch, dust, synth):
     """SGD + momentum and Adam steps over 2^24 fp32 parameters (the order of
     the pages' 8 x 512 model)."""
     n = 1 << 24
-    W = torch.randn(n, device="cuda:0")
-    G = torch.randn(n, device="cuda:0")
+    gen = torch.Generator(device="cuda:0").manual_seed(13)
+    W = torch.randn(n, device="cuda:0", generator=gen)
+    G = torch.randn(n, device="cuda:0", generator=gen)
     m = torch.zeros(n, device="cuda:0")
     v = torch.zeros(n, device="cuda:0")
     ms_sgd = _time_calls(torch, lambda: dust.sgd_momentum_(W, G, m, lr=1e-3, momentum=0.9),
