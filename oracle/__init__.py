@@ -69,16 +69,16 @@ def _load():
     opt = ctypes.c_void_p
     lib.oracle_head_estimate.argtypes = [_f64p, _i32p, _f64p, _i64, _i64, _i64, _i64,
                                          _f64, _i64, _f64, _u64, _u32,
-                                         _f64p, _f64p, opt, opt, opt, opt]
+                                         _f64p, _f64p, opt, opt, opt, opt, opt]
     lib.oracle_head_estimate.restype = ctypes.c_int
     lib.oracle_head_rows.argtypes = [_f64p, _i32p, _i64, _i64, _i64, _f64, _i64, _f64,
-                                     _u64, _u32, _i64p, _i64, _f64p, opt]
+                                     _u64, _u32, _i64p, _i64, _f64p, opt, opt]
     lib.oracle_head_rows.restype = ctypes.c_int
     lib.oracle_linear_estimate.argtypes = [_f64p, _f64p, _i64, _i64, _i64, _i64, _f64,
-                                           _i64, _f64, _u64, _u32, _f64p, _f64p, opt]
+                                           _i64, _f64, _u64, _u32, _f64p, _f64p, opt, opt]
     lib.oracle_linear_estimate.restype = ctypes.c_int
     lib.oracle_linear_rows.argtypes = [_f64p, _i64, _i64, _i64, _f64, _i64, _f64, _u64,
-                                       _u32, _i64p, _i64, _f64p]
+                                       _u32, _i64p, _i64, _f64p, opt]
     lib.oracle_linear_rows.restype = ctypes.c_int
     lib.oracle_perturbed_linear.argtypes = [_f64p, _f64p, _i64, _i64, _i64, _f64, _u64, _u32,
                                             _i64, _i64, _f64p]
@@ -170,7 +170,8 @@ def head_estimate(logits, targets, X, seq_len: int, sigma: float, K: int, gamma:
     section), then the credit assignment of the paper digest, section 2.2.
 
     Returns (g_hat [T,V], G_W [V,d]) and, with diagnostics, a dict with
-    ell [K,T], c [K,T], r [K,T], ell0 [T]."""
+    ell [K,T], c [K,T], r [K,T], ell0 [T] and g_scale [T,V], the magnitude
+    (1/(K sigma)) sum_i |r_i a_i| of the terms each element of g_hat sums."""
     z = _f64c(logits)
     y = np.ascontiguousarray(np.asarray(targets, dtype=np.int32))
     Xd = _f64c(X)
@@ -181,39 +182,47 @@ def head_estimate(logits, targets, X, seq_len: int, sigma: float, K: int, gamma:
     diag = None
     if diagnostics:
         diag = {"ell": np.empty((K, T)), "c": np.empty((K, T)), "r": np.empty((K, T)),
-                "ell0": np.empty(T)}
+                "ell0": np.empty(T), "g_scale": np.empty((T, V))}
     rc = _load().oracle_head_estimate(
         z, y, Xd, T, V, d, int(seq_len), float(sigma), int(K), float(gamma),
         int(seed), int(stream), g, G,
         _ptr(diag["ell"]) if diag else None, _ptr(diag["c"]) if diag else None,
-        _ptr(diag["r"]) if diag else None, _ptr(diag["ell0"]) if diag else None)
+        _ptr(diag["r"]) if diag else None, _ptr(diag["ell0"]) if diag else None,
+        _ptr(diag["g_scale"]) if diag else None)
     if rc != 0:
         raise ValueError("oracle_head_estimate rejected its arguments")
     return (g, G, diag) if diagnostics else (g, G)
 
 
 def head_rows(logits, targets, seq_len: int, sigma: float, K: int, gamma: float,
-              seed: int, tokens, stream: int = 0, with_losses: bool = False):
+              seed: int, tokens, stream: int = 0, with_losses: bool = False,
+              with_scale: bool = False):
     """Error-estimate rows g_hat[tokens, :] of the LM-head estimator, computed
-    token by token (same steps as head_estimate)."""
+    token by token (same steps as head_estimate).  With with_losses the
+    per-draw losses [K, n] follow; with with_scale the term magnitudes
+    (1/(K sigma)) sum_i |r_i a_i| of the same rows [n, V] come last."""
     z = _f64c(logits)
     y = np.ascontiguousarray(np.asarray(targets, dtype=np.int32))
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     T, V = z.shape
     rows = np.empty((tok.shape[0], V), dtype=np.float64)
     ell = np.empty((K, tok.shape[0]), dtype=np.float64) if with_losses else None
+    scale = np.empty_like(rows) if with_scale else None
     rc = _load().oracle_head_rows(z, y, T, V, int(seq_len), float(sigma), int(K),
                                   float(gamma), int(seed), int(stream), tok, tok.shape[0],
-                                  rows, _ptr(ell))
+                                  rows, _ptr(ell), _ptr(scale))
     if rc != 0:
         raise ValueError("oracle_head_rows rejected its arguments")
-    return (rows, ell) if with_losses else rows
+    out = (rows,) + ((ell,) if with_losses else ()) + ((scale,) if with_scale else ())
+    return out if len(out) > 1 else rows
 
 
 def linear_estimate(X, c, seq_len: int, N: int, sigma: float, gamma: float, seed: int,
-                    stream: int = 0, with_r: bool = False):
+                    stream: int = 0, with_r: bool = False, with_scale: bool = False):
     """Hidden linear layer: caller's centred loss decreases c [K,T] -> reward scan,
-    error estimate and outer product (paper digest, section 2.2)."""
+    error estimate and outer product (paper digest, section 2.2).  Returns
+    (g_hat, G_W), then r [K,T] with with_r, then the term magnitudes of g_hat
+    [T,N] with with_scale."""
     Xd = _f64c(X)
     cd = _f64c(c)
     K, T = cd.shape
@@ -221,27 +230,30 @@ def linear_estimate(X, c, seq_len: int, N: int, sigma: float, gamma: float, seed
     g = np.empty((T, N), dtype=np.float64)
     G = np.empty((N, d_in), dtype=np.float64)
     r = np.empty((K, T), dtype=np.float64) if with_r else None
+    scale = np.empty_like(g) if with_scale else None
     rc = _load().oracle_linear_estimate(Xd, cd, T, d_in, int(N), int(seq_len), float(sigma),
                                         int(K), float(gamma), int(seed), int(stream), g, G,
-                                        _ptr(r))
+                                        _ptr(r), _ptr(scale))
     if rc != 0:
         raise ValueError("oracle_linear_estimate rejected its arguments")
-    return (g, G, r) if with_r else (g, G)
+    return (g, G) + ((r,) if with_r else ()) + ((scale,) if with_scale else ())
 
 
 def linear_rows(c, seq_len: int, N: int, sigma: float, gamma: float, seed: int, tokens,
-                stream: int = 0):
-    """Error-estimate rows g_hat[tokens, :] of the linear-layer estimator."""
+                stream: int = 0, with_scale: bool = False):
+    """Error-estimate rows g_hat[tokens, :] of the linear-layer estimator (and,
+    with with_scale, the term magnitudes of the same rows)."""
     cd = _f64c(c)
     K, T = cd.shape
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     rows = np.empty((tok.shape[0], N), dtype=np.float64)
+    scale = np.empty_like(rows) if with_scale else None
     rc = _load().oracle_linear_rows(cd, T, int(N), int(seq_len), float(sigma), int(K),
                                     float(gamma), int(seed), int(stream), tok, tok.shape[0],
-                                    rows)
+                                    rows, _ptr(scale))
     if rc != 0:
         raise ValueError("oracle_linear_rows rejected its arguments")
-    return rows
+    return (rows, scale) if with_scale else rows
 
 
 def perturbed_linear(X, W, sigma: float, seed: int, stream: int = 0, draw0: int = 0,

@@ -191,19 +191,26 @@ void oracle_reward_scan(const double* c, int64_t K, int64_t T, int64_t L, double
 
 /* Error estimate of token t ([P2] section 2.2):
  * g_t = -(1/(K sigma)) sum_i r^(i)_t a^(i)_t, a regenerated from its counters.
- * r^(i)_t is read at r[i * r_stride + r_col]; t keys the noise. */
+ * r^(i)_t is read at r[i * r_stride + r_col]; t keys the noise.
+ * s_row (NULL to skip) receives the magnitude of the same sum's terms,
+ * (1/(K sigma)) sum_i |r^(i)_t a^(i)_t|, the scale that a rounding error in
+ * any one term is measured against; it does not enter g. */
 static void error_estimate_token(const double* r, int64_t K, int64_t r_stride, int64_t r_col,
                                  int64_t t, int64_t N, double sigma, uint64_t seed,
-                                 uint32_t stream, double* g_row, double* a_scratch)
+                                 uint32_t stream, double* g_row, double* a_scratch,
+                                 double* s_row)
 {
     for (int64_t n = 0; n < N; ++n) g_row[n] = 0.0;
+    if (s_row) for (int64_t n = 0; n < N; ++n) s_row[n] = 0.0;
     for (int64_t i = 0; i < K; ++i) {
         double rit = r[i * r_stride + r_col];
         noise_row(seed, stream, i, t, N, a_scratch);
         for (int64_t n = 0; n < N; ++n) g_row[n] += rit * a_scratch[n];
+        if (s_row) for (int64_t n = 0; n < N; ++n) s_row[n] += fabs(rit * a_scratch[n]);
     }
     double scale = -1.0 / ((double)K * sigma);
     for (int64_t n = 0; n < N; ++n) g_row[n] *= scale;
+    if (s_row) for (int64_t n = 0; n < N; ++n) s_row[n] *= -scale;
 }
 
 /* Weight gradient ([P2] section 2.2): G_W[n][k] = sum_t g[t][n] * X[t][k]. */
@@ -232,7 +239,8 @@ int oracle_head_estimate(const double* logits, const int32_t* targets, const dou
                          double sigma, int64_t K, double gamma,
                          uint64_t seed, uint32_t stream,
                          double* g_hat, double* G_W,
-                         double* ell_out, double* c_out, double* r_out, double* ell0_out)
+                         double* ell_out, double* c_out, double* r_out, double* ell0_out,
+                         double* g_scale_out)
 {
     if (T <= 0 || V <= 0 || V % 4 != 0 || d <= 0 || K <= 0 || L <= 0 || T % L != 0)
         return -1;
@@ -266,7 +274,8 @@ int oracle_head_estimate(const double* logits, const int32_t* targets, const dou
         double* a = (double*)malloc(sizeof(double) * (size_t)V);
         #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < T; ++t)
-            error_estimate_token(r, K, T, t, t, V, sigma, seed, stream, g_hat + t * V, a);
+            error_estimate_token(r, K, T, t, t, V, sigma, seed, stream, g_hat + t * V, a,
+                                 g_scale_out ? g_scale_out + t * V : NULL);
         free(a);
     }
     /* weight gradient */
@@ -284,13 +293,14 @@ int oracle_head_estimate(const double* logits, const int32_t* targets, const dou
 /* LM-head error-estimate rows for a subset of tokens (for full-size checks).*/
 /* Token t's row needs the losses of tokens t .. end of its sequence when    */
 /* gamma > 0 (and of token t alone when gamma = 0); only those are computed. */
-/* rows [n_tok, V]; ell_rows [K, n_tok] (may be NULL).                        */
+/* rows [n_tok, V]; ell_rows [K, n_tok] and scale_rows [n_tok, V] (term      */
+/* magnitudes, see error_estimate_token) may be NULL.                        */
 /* ------------------------------------------------------------------------- */
 int oracle_head_rows(const double* logits, const int32_t* targets,
                      int64_t T, int64_t V, int64_t L,
                      double sigma, int64_t K, double gamma, uint64_t seed, uint32_t stream,
                      const int64_t* tokens, int64_t n_tok,
-                     double* rows, double* ell_rows)
+                     double* rows, double* ell_rows, double* scale_rows)
 {
     if (T <= 0 || V <= 0 || V % 4 != 0 || K <= 0 || L <= 0 || T % L != 0) return -1;
     for (int64_t q = 0; q < n_tok; ++q)
@@ -328,7 +338,8 @@ int oracle_head_rows(const double* logits, const int32_t* targets,
                 /* the suffix t .. seg_end-1 is one (truncated) sequence */
                 oracle_reward_scan(c, K, span, span, gamma, r);
                 /* r of token t is column 0 of the [K, span] array */
-                error_estimate_token(r, K, span, 0, t, V, sigma, seed, stream, rows + q * V, a);
+                error_estimate_token(r, K, span, 0, t, V, sigma, seed, stream, rows + q * V, a,
+                                     scale_rows ? scale_rows + q * V : NULL);
             }
         }
         free(a); free(zp); free(ell); free(c); free(r);
@@ -346,7 +357,7 @@ int oracle_linear_estimate(const double* X, const double* c,
                            int64_t T, int64_t d_in, int64_t N, int64_t L,
                            double sigma, int64_t K, double gamma,
                            uint64_t seed, uint32_t stream,
-                           double* g_hat, double* G_W, double* r_out)
+                           double* g_hat, double* G_W, double* r_out, double* g_scale_out)
 {
     if (T <= 0 || N <= 0 || N % 4 != 0 || d_in <= 0 || K <= 0 || L <= 0 || T % L != 0)
         return -1;
@@ -358,7 +369,8 @@ int oracle_linear_estimate(const double* X, const double* c,
         double* a = (double*)malloc(sizeof(double) * (size_t)N);
         #pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < T; ++t)
-            error_estimate_token(r, K, T, t, t, N, sigma, seed, stream, g_hat + t * N, a);
+            error_estimate_token(r, K, T, t, t, N, sigma, seed, stream, g_hat + t * N, a,
+                                 g_scale_out ? g_scale_out + t * N : NULL);
         free(a);
     }
     oracle_outer_sum(g_hat, X, T, N, d_in, G_W);
@@ -368,10 +380,11 @@ int oracle_linear_estimate(const double* X, const double* c,
 }
 
 /* Linear-layer error-estimate rows for a subset of tokens; r is scanned
- * from the caller's c over the whole [K,T] array first. rows [n_tok, N]. */
+ * from the caller's c over the whole [K,T] array first. rows [n_tok, N];
+ * scale_rows [n_tok, N] (term magnitudes) may be NULL. */
 int oracle_linear_rows(const double* c, int64_t T, int64_t N, int64_t L,
                        double sigma, int64_t K, double gamma, uint64_t seed, uint32_t stream,
-                       const int64_t* tokens, int64_t n_tok, double* rows)
+                       const int64_t* tokens, int64_t n_tok, double* rows, double* scale_rows)
 {
     if (T <= 0 || N <= 0 || N % 4 != 0 || K <= 0 || L <= 0 || T % L != 0) return -1;
     for (int64_t q = 0; q < n_tok; ++q)
@@ -385,7 +398,7 @@ int oracle_linear_rows(const double* c, int64_t T, int64_t N, int64_t L,
         #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < n_tok; ++q)
             error_estimate_token(r, K, T, tokens[q], tokens[q], N, sigma, seed, stream,
-                                 rows + q * N, a);
+                                 rows + q * N, a, scale_rows ? scale_rows + q * N : NULL);
         free(a);
     }
     free(r);

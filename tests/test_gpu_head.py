@@ -1,5 +1,8 @@
 """dust_head_estimate (LM head on cached logits) against the oracle: g_hat and
-G_W within relative L2 1e-3 / cosine 0.99999, per-draw losses within 2e-4 nats.
+G_W within relative L2 1e-3 / cosine 0.99999 as whole arrays and g_hat row by
+row, every element of g_hat within 1e-4 of the magnitude of the terms it sums
+and every element of G_W within 8 x 2^-11 of its root-sum-square scale, and
+per-draw losses within 2e-4 nats.
 
 Covers the fused gamma = 0 kernel at every vocabulary layout it has (one wave
 per token with 4..64 columns per lane, 2 and 4 waves with logits in LDS, 8 waves
@@ -11,7 +14,8 @@ import pytest
 
 import oracle
 from activation_perturbation_estimator_amd import synth
-from util import assert_parity, need_gpu
+from util import (G_HAT_TERM_TOL, assert_elementwise, assert_gw, assert_parity, assert_rows,
+                  need_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +34,10 @@ def _check(z, y, X, *, sigma, K, gamma, seed, seq_len, stream=0):
     rg, rG, diag = oracle.head_estimate(synth.to_f64(z), y.numpy(), synth.to_f64(X), seq_len,
                                         sigma, K, gamma, seed, stream, diagnostics=True)
     assert_parity(g, rg, "g_hat")
+    assert_rows(g, rg, "g_hat rows")
+    assert_elementwise(g, rg, diag["g_scale"], "g_hat elements", G_HAT_TERM_TOL)
     assert_parity(G, rG, "G_W")
+    assert_gw(G, rg, synth.to_f64(X))
     err = np.abs(ell - diag["ell"]).max()
     assert err <= 2e-4, err
     return g, G

@@ -7,7 +7,8 @@ import pytest
 
 import oracle
 from activation_perturbation_estimator_amd import synth
-from util import assert_parity, need_gpu
+from util import (G_HAT_TERM_TOL, assert_elementwise, assert_gw, assert_parity, assert_rows,
+                  need_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,10 +29,13 @@ def test_linear_matches_oracle(T, L, d, N, K, gamma, bf16):
     X, c = synth.linear_inputs(T, d, K, seed=T + N, c_seed=K, bf16=bf16)
     sigma, seed, stream = 0.01, 9, 1
     g, G = _run(dust, X, c, N=N, sigma=sigma, gamma=gamma, seed=seed, seq_len=L, stream=stream)
-    rg, rG = oracle.linear_estimate(synth.to_f64(X), c.double().numpy(), L, N, sigma, gamma, seed,
-                                    stream)
+    rg, rG, sc = oracle.linear_estimate(synth.to_f64(X), c.double().numpy(), L, N, sigma, gamma,
+                                        seed, stream, with_scale=True)
     assert_parity(g, rg, "g_hat")
+    assert_rows(g, rg, "g_hat rows")
+    assert_elementwise(g, rg, sc, "g_hat elements", G_HAT_TERM_TOL)
     assert_parity(G, rG, "G_W")
+    assert_gw(G, rg, synth.to_f64(X))
 
 
 def test_one_hot_closed_form():
@@ -48,6 +52,12 @@ def test_one_hot_closed_form():
         for t in range((s_s // L) * L, s_s + 1):
             ref[t] = -(gamma ** (s_s - t)) * a[i_s, t] / (K * sigma)
         assert_parity(g, ref, "g_hat one-hot")
+        inside = ~np.all(ref == 0, axis=1)
+        assert_rows(g[inside], ref[inside], "g_hat one-hot rows")
+        # one term per element: within fp32 rounding of the scan's powers of
+        # gamma, plus the normals' own accuracy (1e-5 absolute) times 1/(K sigma)
+        assert_elementwise(g, ref, np.abs(ref), "g_hat one-hot elements", 1e-5,
+                           atol=1e-5 / (K * sigma))
         outside = np.ones(T, bool)
         outside[(s_s // L) * L:s_s + 1] = False
         assert np.all(g[outside] == 0)

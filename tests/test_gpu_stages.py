@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from activation_perturbation_estimator_amd import synth
-from util import assert_parity, need_gpu, rel_l2
+from util import (G_HAT_TERM_TOL, assert_elementwise, assert_parity, assert_rows, need_gpu,
+                  rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,8 +102,12 @@ def test_error_estimate(K, T, N, L, gamma):
     g = dust.error_estimate(_cuda(torch.from_numpy(r.astype(np.float32))), N=N, sigma=sigma,
                             seed=seed, stream=stream)
     torch.cuda.synchronize()
-    ref = oracle.linear_rows(c, L, N, sigma, gamma, seed, list(range(T)), stream)
-    assert_parity(g.cpu().numpy(), ref, "g_hat")
+    ref, sc = oracle.linear_rows(c, L, N, sigma, gamma, seed, list(range(T)), stream,
+                                 with_scale=True)
+    got = g.cpu().numpy()
+    assert_parity(got, ref, "g_hat")
+    assert_rows(got, ref, "g_hat rows")
+    assert_elementwise(got, ref, sc, "g_hat elements", G_HAT_TERM_TOL)
 
 
 @pytest.mark.parametrize("T,N,d,bf16", [(600, 1000, 72, True), (600, 1000, 72, False),
