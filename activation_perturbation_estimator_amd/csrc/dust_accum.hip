@@ -12,6 +12,7 @@
 // of 64 draws are fetched at once (lane l holds draw i0+l) and broadcast one at
 // a time with v_readlane.
 #include "dust_device.hpp"
+#include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
 
 namespace dust {
@@ -19,8 +20,10 @@ namespace dust {
 template <int kNB, int kW>
 __global__ void __launch_bounds__(64 * kW)
 error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t N, float scale,
-                      uint32_t stream, uint32_t k0, uint32_t k1, float* __restrict__ g_hat) {
+                      uint32_t stream, uint32_t k0, uint32_t k1, float* __restrict__ g_hat,
+                      Gemm16Out op) {
   constexpr int kCols = 4 * kNB;
+  __shared__ float red[3 * kW];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t t = blockIdx.x;
@@ -48,31 +51,37 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
   }
   float* grow = g_hat + t * N;
 #pragma unroll
+  for (int q = 0; q < kCols; ++q) acc[q] *= scale;
+#pragma unroll
   for (int b = 0; b < kNB; ++b) {
     const int64_t j = (int64_t)b * 64 * kW + wave * 64 + lane;
     if (j < nblk)
       *reinterpret_cast<float4*>(grow + 4 * j) =
-          make_float4(acc[4 * b] * scale, acc[4 * b + 1] * scale, acc[4 * b + 2] * scale,
-                      acc[4 * b + 3] * scale);
+          make_float4(acc[4 * b], acc[4 * b + 1], acc[4 * b + 2], acc[4 * b + 3]);
   }
+  // The fp16 operands of the G_W pass: this workgroup owns the token's whole row.
+  if (op.g16 != nullptr) emit_operands<kNB, kW>(op, t, N, acc, red);
 }
 
 template <int kNB, int kW>
 static hipError_t launch_ee_t(const float* r, int64_t K, int64_t T, int64_t N, float scale,
-                              uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s) {
+                              uint32_t stream, uint64_t seed, float* g_hat, const Gemm16Out& op,
+                              hipStream_t s) {
   hipLaunchKernelGGL((error_estimate_kernel<kNB, kW>), dim3((uint32_t)T), dim3(64 * kW), 0, s, r,
-                     K, T, N, scale, stream, (uint32_t)seed, (uint32_t)(seed >> 32), g_hat);
+                     K, T, N, scale, stream, (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, op);
   return hipGetLastError();
 }
 
 hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
-                                 uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s) {
+                                 uint32_t stream, uint64_t seed, float* g_hat,
+                                 const Gemm16Out& op, hipStream_t s) {
   if (T == 0) return hipSuccess;
   // the noise comes divided by kBoxMullerScale (normal4_scaled)
   const float scale = -kBoxMullerScale / ((float)K * sigma);
   const HeadShape h = wide_shape(N);
 #define DUST_EE_CASE(NB, W) \
-  if (h.nb == NB && h.w == W) return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, g_hat, s);
+  if (h.nb == NB && h.w == W)                                                                  \
+    return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, g_hat, op, s);
   DUST_EE_CASE(1, 1)
   DUST_EE_CASE(2, 1)
   DUST_EE_CASE(4, 1)

@@ -141,11 +141,14 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
   void* gemm_ws = ws + align_up(plan.delta_bytes);
   const bool zbf16 = (logits_dt == DUST_BF16);
 
+  // the kernel that finishes g_hat also writes the fp16 operands of the G_W pass
+  const dust::Gemm16Out op = dust::outer_sum_operands(gemm_ws, T, V, d, X, x_dt == DUST_BF16);
+
   hipError_t e = record(stage_events, 0, s);
   if (e != hipSuccess) return DUST_ERR_HIP;
   if (plan.fused) {
     e = dust::launch_head_fused(logits, zbf16, targets, T, V, sigma, K, stream, seed, g_hat,
-                                losses_opt, s);
+                                losses_opt, op, s);
     if (e != hipSuccess) return DUST_ERR_HIP;
     if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
     if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
@@ -158,11 +161,11 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
         (e = dust::launch_reward_scan(delta, K, T, seq_len, gamma, delta, s)) != hipSuccess)
       return DUST_ERR_HIP;
     if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
-    e = dust::launch_error_estimate(delta, K, T, V, sigma, stream, seed, g_hat, s);
+    e = dust::launch_error_estimate(delta, K, T, V, sigma, stream, seed, g_hat, op, s);
     if (e != hipSuccess) return DUST_ERR_HIP;
     if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
   }
-  e = dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, V, d, G_W, gemm_ws, s);
+  e = dust::launch_outer_sum16(op, g_hat, V, G_W, gemm_ws, s);
   if (e != hipSuccess) return DUST_ERR_HIP;
   return hip_status(record(stage_events, 3, s));
 }
@@ -197,11 +200,12 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
     rr = r;
   }
   if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
-  if ((e = dust::launch_error_estimate(rr, K, T, N, sigma, stream, seed, g_hat, s)) != hipSuccess)
+  const dust::Gemm16Out op = dust::outer_sum_operands(gemm_ws, T, N, d_in, X, x_dt == DUST_BF16);
+  if ((e = dust::launch_error_estimate(rr, K, T, N, sigma, stream, seed, g_hat, op, s)) !=
+      hipSuccess)
     return DUST_ERR_HIP;
   if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
-  if ((e = dust::launch_outer_sum(g_hat, X, x_dt == DUST_BF16, T, N, d_in, G_W, gemm_ws, s)) !=
-      hipSuccess)
+  if ((e = dust::launch_outer_sum16(op, g_hat, N, G_W, gemm_ws, s)) != hipSuccess)
     return DUST_ERR_HIP;
   return hip_status(record(stage_events, 3, s));
 }
@@ -252,8 +256,9 @@ dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N,
   if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || !width_ok(N) || !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
   if (T > kMaxTokens || T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
+  const dust::Gemm16Out none{};  // no G_W operands wanted
   return hip_status(
-      dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, g_hat, as_stream(s)));
+      dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, g_hat, none, as_stream(s)));
 }
 
 dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, int64_t T,

@@ -2,76 +2,105 @@
 //
 // Paper digest, section 2.2: the error estimate's outer product with the layer
 // input gives the weight gradient, in the same form as backprop.  As a matrix
-// product, G[m][n] = sum_t g[t][m] X[t][n], contracting over the token axis,
-// which is the slow axis of both row-major operands.
+// product, G[m][n] = sum_t g[t][m] X[t][n], contracting over the token axis.
 //
-// Precision: g is fp32 and the product must keep ~fp32 accuracy.  Each fp32
-// value v is split into two bf16 values hi = bf16(v), lo = bf16(v - hi) with
-// |v - hi - lo| <= 2^-17 |v|, and the products run on the bf16 MFMA units with
-// fp32 accumulation: g_hi X + g_lo X for bf16 X (exact in bf16), plus
-// g_hi X_lo for fp32 X.  Every bf16 x bf16 product is exact in fp32.
+// Precision: one pass of v_mfma_f32_32x32x16_f16 (fp32 accumulation) over the
+// fp16 operand form of dust_gemm16.hpp: every token's rows rescaled by a power
+// of two (exact) and rounded to fp16 (11 significant bits; bf16 X is exact),
+// so each product g_t[m] x_t[n] carries a relative error <= 2^-11 (2^-10 for
+// fp32 X), independent between tokens.  Tokens whose range fits no power of
+// two (or with non-finite values) are added afterwards in fp32 from the
+// original g and X.
 //
-// Data movement: both operands stay in their natural token-major layout.  Each
-// pipeline step moves kBT token rows of a g tile (fp32) and of an X tile (bf16)
-// straight from HBM into LDS with buffer loads that write LDS directly (no
-// registers, hardware bounds checks give zeros past the end), into a ring of
-// kS stages, so kS - 1 steps are in flight while the matrix cores work.  The
-// operands of v_mfma_f32_32x32x16_bf16 want 8 consecutive tokens per lane:
-//   X: ds_read_b64_tr_b16 gives each lane one column of a 4-token x 16-column
-//      block of a token-major tile, two of them make the lane's 8 tokens;
-//   g: eight ds_read_b32 (one per token) of the lane's column, then the hi/lo
-//      split in registers.
-// 16-byte chunks of each LDS row are xor-swizzled by the row index so that both
-// read patterns hit distinct banks.
+// Data movement: the kernel reads only the fp16 operands, written by the
+// kernels that produce g (or by prep16_kernel for a caller's fp32 g):
+//   g16 [T][Mp] token-major: each pipeline step moves 32 token rows of a
+//       256-column tile into LDS; ds_read_b64_tr_b16 gives a lane one column
+//       of a 4-token x 16-column block, two of them the lane's 8 tokens of a
+//       v_mfma_f32_32x32x16_f16 operand.  16-byte chunks of each LDS row are
+//       xor-swizzled by the row index so that the reads hit distinct banks.
+//   x16 [T/8][d][8] blocked: each column's 8 tokens are one 16-byte chunk,
+//       exactly a lane's operand, read with one ds_read_b128.
+// Both go from HBM straight into LDS with buffer loads that write LDS (no
+// registers), into a ring of kS stages, so kS - 1 steps are in flight while
+// the matrix cores work.  Every offset of a load is in its vector offset, so
+// the buffer's bounds check covers all of it: loads past a token split's rows
+// return zeros.
 //
-// Tiling: a workgroup (4 waves, one per SIMD) owns a 128 x 256 tile of G over
+// Tiling: a workgroup (4 waves, one per SIMD) owns a 2 kWM x 256 tile of G over
 // one token range (split-K over tokens so that the grid fills the 256 CUs);
-// each wave owns 64 x 128 as 2 x 4 MFMA blocks.  Partial tiles of the token
-// splits are summed in a fixed order by a second kernel, so results are
-// deterministic.  (Measured on MI355X: 128 x 256 tiles with a 4-stage ring beat
-// 256 x 256 and 128 x 512 tiles; the loop is bound by the VALU work of the
-// hi/lo split and the LDS reads issued between matrix instructions, not by
-// HBM.)
+// each wave owns kWM x 128 as kWM/32 x 4 MFMA blocks.  Partial tiles of the
+// token splits are summed in a fixed order by a second kernel, so results are
+// deterministic.
 #include "dust_device.hpp"
+#include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
+
+// Tile shape of the G_W kernel (see Cfg below): 0 is the built configuration;
+// the others are kept for measurement on other shapes and parts.
+#ifndef DUST_GEMM_CONFIG
+#define DUST_GEMM_CONFIG 1
+#endif
 
 namespace dust {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f16x8_t lds_f16x8;
 
-constexpr int kBM = 128;   // rows of G (layer outputs) per workgroup
-constexpr int kBN = 256;   // columns of G (layer inputs) per workgroup
-constexpr int kWaveM = 64, kWaveN = 128;  // per wave: 2 x 4 blocks of 32 x 32
-constexpr int kMB = kWaveM / 32, kNB = kWaveN / 32;
-constexpr int kXcds = 8;   // MI355X: workgroups go round-robin to 8 XCDs
-constexpr int kGRow = kBM * 4;  // bytes of one token row of the g tile (fp32)
-constexpr int kXRow = kBN * 2;  // bytes of one token row of an X tile (bf16)
-constexpr int kGRowsPerLoad = 1024 / kGRow;  // token rows per 1 KiB load
-constexpr int kXRowsPerLoad = 1024 / kXRow;
-static_assert((kBM / kWaveM) * (kBN / kWaveN) == 4, "four waves per workgroup, 2 x 2");
-static_assert(kGRow >= 256 && kXRow >= 256 && kGRow <= 1024 && kXRow <= 1024, "row swizzles");
+constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 XCDs
 
-// Pipeline shape: tokens per step, stages in the LDS ring, workgroups per CU.
-template <bool kXF32>
-struct Pipe {
-  static constexpr int kBT = 32;
-  static constexpr int kS = kXF32 ? 3 : 4;
-  static constexpr int kWgPerCu = 1;
-  static constexpr int kPlanes = kXF32 ? 2 : 1;
-  static constexpr int kGRegion = kBT * kGRow;   // bytes of g per step
-  static constexpr int kXRegion = kBT * kXRow;   // bytes per X plane per step
-  static constexpr int kStageBytes = kGRegion + kPlanes * kXRegion;
-  static constexpr int kGLoads = kGRegion / 1024 / 4;  // 1 KiB loads per wave
-  static constexpr int kXLoads = kXRegion / 1024 / 4;
-  static constexpr int kLoadsPerStage = kGLoads + kPlanes * kXLoads;
+// A workgroup of kWavesM x kWavesN waves owns a (kWavesM kWM) x (kWavesN kWN)
+// tile of G; each wave owns kWM x kWN as (kWM/32) x (kWN/32) MFMA blocks.  A
+// pipeline step moves kBT tokens of both operands into one of kS LDS stages.
+template <int kWavesM_, int kWavesN_, int kWM_, int kWN_, int kBT_, int kS_>
+struct Cfg {
+  static constexpr int kWavesM = kWavesM_, kWavesN = kWavesN_;
+  static constexpr int kWaves = kWavesM * kWavesN, kThreads = 64 * kWaves;
+  static constexpr int kWM = kWM_, kWN = kWN_;
+  static constexpr int kBM = kWavesM * kWM, kBN = kWavesN * kWN;
+  static constexpr int kMB = kWM / 32, kNB = kWN / 32;
+  static constexpr int kBT = kBT_, kS = kS_;
+  static constexpr int kSub = kBT / 16;           // MFMA k-steps of 16 tokens per step
+  static constexpr int kARow = kBM * 2;           // bytes of one token row of the g tile
+  static constexpr int kARegion = kBT * kARow;    // g bytes per stage
+  static constexpr int kXRegion = (kBT / 8) * kBN * 16;  // x bytes per stage
+  static constexpr int kStage = kARegion + kXRegion;
+  static constexpr int kALoads = kARegion / (1024 * kWaves);  // 1 KiB loads per wave, stage
+  static constexpr int kXLoads = kXRegion / (1024 * kWaves);
+  static constexpr int kLoads = kALoads + kXLoads;
+  static constexpr int kARowsPerLoad = 1024 / kARow;
+  static constexpr int kALanesPerRow = 64 / kARowsPerLoad;  // 16-byte chunks per g-tile row
+  static_assert(kALanesPerRow >= 16, "the row swizzle xors chunk indices with up to 12");
+  static_assert(kARow <= 1024, "a 1 KiB load holds whole g-tile rows");
+  static_assert(kARegion % (1024 * kWaves) == 0 && kXRegion % (1024 * kWaves) == 0,
+                "whole 1 KiB loads per wave");
+  static_assert(kBT % 16 == 0 && kSub >= 2, "at least two MFMA k-steps per pipeline step");
+  static_assert(kS >= 2 && kS <= 4, "ring of 2 to 4 stages");
+  static_assert(kS * kStage <= 160 * 1024, "LDS of one CU");
 };
+
+#if DUST_GEMM_CONFIG == 0
+using GemmCfg = Cfg<2, 2, 128, 128, 32, 4>;
+#elif DUST_GEMM_CONFIG == 1
+using GemmCfg = Cfg<4, 2, 64, 128, 32, 4>;
+#elif DUST_GEMM_CONFIG == 2
+using GemmCfg = Cfg<2, 2, 64, 128, 32, 4>;
+#elif DUST_GEMM_CONFIG == 3
+using GemmCfg = Cfg<2, 2, 64, 128, 64, 3>;
+#elif DUST_GEMM_CONFIG == 4
+using GemmCfg = Cfg<4, 2, 32, 128, 32, 4>;
+#elif DUST_GEMM_CONFIG == 5
+using GemmCfg = Cfg<4, 2, 64, 128, 64, 2>;
+#elif DUST_GEMM_CONFIG == 6
+using GemmCfg = Cfg<2, 2, 128, 128, 64, 2>;
+#elif DUST_GEMM_CONFIG == 7
+using GemmCfg = Cfg<4, 2, 32, 128, 64, 3>;
+#endif
 
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
@@ -93,91 +122,66 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane (the
-// LDS base is taken from m0, so it must be uniform over the wave).
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* lds, int voff,
-                                           int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, soff, 0, 0);
+// LDS base is taken from m0, so it must be uniform over the wave).  The whole
+// offset is the lane's vector offset: a chunk at or past the buffer's size
+// reads as zeros.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voff, 0, 0, 0);
 }
 
-// Two fp32 values -> packed bf16 hi and packed bf16 lo (v_cvt_pk_bf16_f32, round
-// to nearest even): v = hi + lo + O(2^-17 |v|).
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const f32x2_t v = {a, b};
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-  const f32x2_t r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-}
-
-// Token-major copies for the operands the main kernel cannot read in place:
-// X as bf16 planes [T][dp] (dp = d rounded up to 8; hi and, for fp32 X, lo),
-// zero in the padding columns.  One thread per 8 columns of a row, grid-stride.
-template <bool kXF32>
-__global__ void __launch_bounds__(256) x_planes_kernel(const void* __restrict__ Xv, int64_t T,
-                                                       int64_t d, int64_t dp,
-                                                       uint16_t* __restrict__ hi,
-                                                       uint16_t* __restrict__ lo) {
-  const int64_t per_row = dp / 8;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T * per_row; i += stride) {
-    const int64_t t = i / per_row, c0 = (i % per_row) * 8;
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t c = c0 + e;
-      v[e] = 0.f;
-      if (c < d) {
-        if constexpr (kXF32) v[e] = reinterpret_cast<const float*>(Xv)[t * d + c];
-        else v[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(Xv)[t * d + c] << 16);
-      }
-    }
-    uint4 h, l;
-    if constexpr (kXF32) {
-      split2(v[0], v[1], h.x, l.x);
-      split2(v[2], v[3], h.y, l.y);
-      split2(v[4], v[5], h.z, l.z);
-      split2(v[6], v[7], h.w, l.w);
-      *reinterpret_cast<uint4*>(lo + t * dp + c0) = l;
-    } else {
-      h.x = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
-      h.y = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xFFFF0000u);
-      h.z = (__float_as_uint(v[4]) >> 16) | (__float_as_uint(v[5]) & 0xFFFF0000u);
-      h.w = (__float_as_uint(v[6]) >> 16) | (__float_as_uint(v[7]) & 0xFFFF0000u);
-    }
-    *reinterpret_cast<uint4*>(hi + t * dp + c0) = h;
+// fp16 operand form of a caller's fp32 g (dust_outer_sum): one workgroup of
+// 256 threads per token, the same scale rule as the producer kernels.
+__global__ void __launch_bounds__(256) prep16_kernel(const float* __restrict__ g, int64_t N,
+                                                     Gemm16Out o) {
+  __shared__ float red[12];
+  const int64_t t = blockIdx.x;
+  const float* grow = g + t * N;
+  float gm = 0.f, xm = 0.f, nf = 0.f;
+  for (int64_t c = threadIdx.x; c < N; c += 256) {
+    const float v = grow[c];
+    gm = fmaxf(gm, __builtin_fabsf(v));
+    if (not_finite(v)) nf = 1.f;
   }
-}
-
-// g [T][N] -> [T][Np] (Np = N rounded up to 4), zero padding; only for N % 4 != 0.
-__global__ void __launch_bounds__(256) g_pad_kernel(const float* __restrict__ g, int64_t T,
-                                                    int64_t N, int64_t Np, float* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < T * Np; i += stride) {
-    const int64_t t = i / Np, c = i % Np;
-    out[i] = c < N ? g[t * N + c] : 0.f;
+  for (int64_t k = threadIdx.x; k < o.d; k += 256) {
+    const float v = load_x(o.X, o.x_bf16, t * o.d + k);
+    xm = fmaxf(xm, __builtin_fabsf(v));
+    if (not_finite(v)) nf = 1.f;
   }
+  gm = wave_max(gm);
+  xm = wave_max(xm);
+  nf = wave_max(nf);
+  group_max3<4>(gm, xm, nf, red);
+  int s;
+  const int mode = choose_scale(gm, xm, nf > 0.f, s);
+  uint16_t* out = o.g16 + t * o.Mp;
+  for (int64_t c = threadIdx.x; c < o.Mp; c += 256)
+    out[c] = (mode == 0 && c < N) ? f16_bits(__builtin_ldexpf(grow[c], -s)) : (uint16_t)0;
+  emit_x_row(o, t, mode, s, 256);
+  if (threadIdx.x == 0) o.flags[t] = mode == 2 ? 1 : 0;
 }
 
-struct GemmGeom {
-  int64_t M, Mp, Nd, dp, T, tiles_m, tiles_n, nsplit, t_per_split, groups, groups_per_xcd;
+struct Gemm16Geom {
+  int64_t M, Mp, d, T, tiles_m, tiles_n, nsplit, t_per_split, groups, groups_per_xcd;
+  int64_t pstride;  // elements between the partial tiles of consecutive splits
 };
 
-template <bool kXF32>
-__global__ void __launch_bounds__(256, Pipe<kXF32>::kWgPerCu)
-outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xh,
-                 const uint16_t* __restrict__ xl, GemmGeom geo, float* __restrict__ out) {
-  using P = Pipe<kXF32>;
-  constexpr int kBT = P::kBT, kS = P::kS;
+template <typename C>
+__global__ void __launch_bounds__(C::kThreads, 1)
+gemm16_kernel(const uint16_t* __restrict__ g16, const uint16_t* __restrict__ x16,
+              const uint8_t* __restrict__ flags, Gemm16Geom geo, float* __restrict__ part,
+              int32_t* __restrict__ list, int32_t* __restrict__ count) {
+  constexpr int kBT = C::kBT, kS = C::kS, kMB = C::kMB, kNB = C::kNB, kWM = C::kWM;
   // One array per ring stage: the compiler tracks the loads into each array
   // separately, so reading one stage waits only for the loads into that stage.
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[P::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[P::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kS > 2 ? P::kStageBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kS > 3 ? P::kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kS > 2 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[kS > 3 ? C::kStage : 16];
   lds_u8* const stages[4] = {(lds_u8*)st0, (lds_u8*)st1, (lds_u8*)st2, (lds_u8*)st3};
 
   // XCD-aware order (workgroup ids go round-robin over the 8 XCDs): each XCD
   // takes a contiguous range of (m tile, split) groups, split-major, so an XCD
-  // works on as few token ranges as possible and reads their X rows from its
+  // works on as few token ranges as possible and reads their x rows from its
   // own L2; the tiles_n workgroups of one group share its g rows there too.
   const int64_t id = blockIdx.x;
   const int64_t xcd = id % kXcds, rank = id / kXcds;
@@ -185,80 +189,90 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xh,
   if (group >= geo.groups) return;  // padding workgroup: leaves before any barrier
   const int64_t ntile = rank % geo.tiles_n;
   const int64_t mtile = group % geo.tiles_m, split = group / geo.tiles_m;
-  const int m0 = (int)(mtile * kBM), n0 = (int)(ntile * kBN);
-  const int64_t t_begin = split * geo.t_per_split;
+  const int m0 = (int)(mtile * C::kBM), n0 = (int)(ntile * C::kBN);
+  const int64_t t_begin = split * geo.t_per_split;  // a multiple of 8
   const int64_t t_end = min(geo.T, t_begin + geo.t_per_split);
+  const int64_t t_rows = t_end - t_begin;
   // Whole ring turns: the last split's extra steps read zeros.
-  const int nsteps = (int)((t_end - t_begin + kS * kBT - 1) / (kS * kBT)) * kS;
+  const int nsteps = (int)((t_rows + kS * kBT - 1) / (kS * kBT)) * kS;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
 
-  // Buffer resources over this split's token rows: loads past t_end read 0.
-  // Columns past M (or d) in the last tile read the next row's values, which
-  // reach only accumulator rows (columns) that are never stored.
-  const int64_t t_rows = t_end - t_begin;
-  const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(g + t_begin * geo.Mp), 0, (int)(t_rows * geo.Mp * 4), 0x00020000);
-  const __amdgpu_buffer_rsrc_t xh_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(xh + t_begin * geo.dp), 0, (int)(t_rows * geo.dp * 2), 0x00020000);
-  __amdgpu_buffer_rsrc_t xl_rsrc = xh_rsrc;
-  if constexpr (kXF32)
-    xl_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xl + t_begin * geo.dp), 0,
-                                                (int)(t_rows * geo.dp * 2), 0x00020000);
-
-  // Loads: a 1 KiB load of a wave fills whole token rows of one tile; lane l
-  // fetches the 16-byte chunk that lands at LDS position l.
-  int g_voff[P::kGLoads], x_voff[P::kXLoads];
+  // The split's flags (4 per word; bytes past the split read as 0), the first
+  // kEarlyWords words per thread loaded now by the workgroup that lists them.
+  const bool lister = (mtile == 0 && ntile == 0);
+  auto flag_word = [&](int64_t i) -> uint32_t {  // flags of tokens t_begin + i .. + 3
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(flags + t_begin + i);
+    return (t_rows - i >= 4) ? v : (v & ((1u << (8 * (t_rows - i))) - 1u));
+  };
+  constexpr int kEarlyWords = (2048 / 4 + C::kThreads - 1) / C::kThreads;
+  uint32_t fbits = 0u;
+  if (lister) {
 #pragma unroll
-  for (int i = 0; i < P::kGLoads; ++i) {
-    constexpr int kLanesPerRow = 64 / kGRowsPerLoad;
-    const int row = (wave * P::kGLoads + i) * kGRowsPerLoad + lane / kLanesPerRow;
-    const int gc = (lane % kLanesPerRow) ^ (((row >> 3) & 1) << 3);  // chunk = 4 fp32 columns
-    g_voff[i] = (int)((row * geo.Mp + m0 + 4 * gc) * 4);
-  }
-#pragma unroll
-  for (int i = 0; i < P::kXLoads; ++i) {
-    constexpr int kLanesPerRow = 64 / kXRowsPerLoad;
-    const int row = (wave * P::kXLoads + i) * kXRowsPerLoad + lane / kLanesPerRow;
-    const int xc = (lane % kLanesPerRow) ^ ((row & 3) << 2);  // chunk = 8 bf16 columns
-    x_voff[i] = (int)((row * geo.dp + n0 + 8 * xc) * 2);
-  }
-  auto issue = [&](lds_u8* st, int step) {
-    const int tl = step * kBT;
-    const int g_soff = (int)(tl * geo.Mp * 4), x_soff = (int)(tl * geo.dp * 2);
-#pragma unroll
-    for (int i = 0; i < P::kGLoads; ++i)
-      load_lds16(g_rsrc, st + (wave * P::kGLoads + i) * 1024, g_voff[i], g_soff);
-#pragma unroll
-    for (int i = 0; i < P::kXLoads; ++i) {
-      const int blk = P::kGRegion + (wave * P::kXLoads + i) * 1024;
-      load_lds16(xh_rsrc, st + blk, x_voff[i], x_soff);
-      if constexpr (kXF32) load_lds16(xl_rsrc, st + P::kXRegion + blk, x_voff[i], x_soff);
+    for (int w = 0; w < kEarlyWords; ++w) {
+      const int64_t i = ((int64_t)w * C::kThreads + tid) * 4;
+      if (i < t_rows) fbits |= flag_word(i);
     }
+  }
+
+  // Buffer resources over this split's rows of g16 and token groups of x16.
+  // Columns past M (or d) in the last tile read the next row's (group's)
+  // values, which reach only accumulator rows (columns) that are never stored.
+  const int64_t Mp = geo.Mp, d = geo.d;
+  const __amdgpu_buffer_rsrc_t g_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(g16 + t_begin * Mp), 0, (int)(t_rows * Mp * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x16 + (t_begin >> 3) * d * 8), 0, (int)(((t_rows + 7) >> 3) * d * 16),
+      0x00020000);
+
+  // Load offsets at step 0; a 1 KiB load of a wave fills whole token rows of
+  // the g tile (lane l fetches the chunk that lands at LDS position l), or 64
+  // consecutive column chunks of one token group of the x tile.
+  int a_voff[C::kALoads], x_voff[C::kXLoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int row = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kALanesPerRow;
+    const int gc = (lane % C::kALanesPerRow) ^ ((row & 3) << 2);  // chunk = 8 fp16 columns
+    a_voff[i] = (int)((row * Mp + m0 + 8 * gc) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kXLoads; ++i) {
+    const int chunk = (wave * C::kXLoads + i) * 64 + lane;
+    const int grp = chunk / C::kBN, col = chunk % C::kBN;
+    x_voff[i] = (int)((grp * d + n0 + col) * 16);
+  }
+  const int a_step = (int)(kBT * Mp * 2), x_step = (int)((kBT / 8) * d * 16);
+  auto issue = [&](lds_u8* st, int step) {
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i)
+      load_lds16(g_rsrc, st + (wave * C::kALoads + i) * 1024, a_voff[i] + step * a_step);
+#pragma unroll
+    for (int i = 0; i < C::kXLoads; ++i)
+      load_lds16(x_rsrc, st + C::kARegion + (wave * C::kXLoads + i) * 1024,
+                 x_voff[i] + step * x_step);
   };
 
-  // Fragment addresses (bytes within a stage, for kk = 0).
-  //   g: lane reads column m = wm*128 + mb*32 + lane%32 of tokens 8*(lane/32) + e.
-  //   X: lane group q = lane/16 reads tokens 8*(q/2) + 4*hh + (j/4) (j = lane%16)
-  //      at columns wn*128 + nb*32 + 16*(q%2) + 4*(j%4) .. +3; the transposed read
-  //      returns column wn*128 + nb*32 + lane%32 for tokens 8*(lane/32) + 4*hh + 0..3.
+  // Fragment addresses (bytes within a stage, first 16 tokens).
+  //   g: lane group q = lane/16 reads tokens 8*(q/2) + (j/4) (j = lane%16), and
+  //      4 tokens later, at columns wm*kWM + mb*32 + 16*(q%2) + 4*(j%4) .. +3;
+  //      the transposed reads return column wm*kWM + mb*32 + lane%32 for tokens
+  //      8*(lane/32) + 0..7.
+  //   x: lane reads the chunk of token group lane/32 and column
+  //      wn*128 + nb*32 + lane%32: tokens 8*(lane/32) + 0..7 of that column.
   int a_off[kMB], b_off[kNB];
   {
-    const int h = lane >> 5;
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int m = wm * kWaveM + mb * 32 + (lane & 31);
-      a_off[mb] = (8 * h) * kGRow + (((m >> 2) ^ (h << 3)) << 4) + (m & 3) * 4;
-    }
     const int q = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
+    for (int mb = 0; mb < kMB; ++mb) {
       const int t = 8 * (q >> 1) + (j >> 2);
-      const int n = wn * kWaveN + nb * 32 + 16 * (q & 1) + 4 * (j & 3);
-      b_off[nb] = P::kGRegion + t * kXRow + (((n >> 3) ^ ((j >> 2) << 2)) << 4) + (n & 7) * 2;
+      const int m = wm * kWM + mb * 32 + 16 * (q & 1) + 4 * (j & 3);
+      a_off[mb] = t * C::kARow + (((m >> 3) ^ ((j >> 2) << 2)) << 4) + (m & 7) * 2;
     }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+      b_off[nb] = C::kARegion + ((lane >> 5) * C::kBN + wn * C::kWN + nb * 32 + (lane & 31)) * 16;
   }
 
   f32x16_t acc[kMB][kNB];
@@ -269,92 +283,96 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xh,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // Operands of 16 tokens: g as read (fp32, split just before use, so that the
-  // reads stay in flight behind earlier matrix work) and X as bf16 fragments.
   struct Frag {
-    float a[kMB][8];
-    bf16x8_t bh[kNB], bl[kXF32 ? kNB : 1];
+    f16x4_t a[kMB][2];  // tokens 0..3 and 4..7 of the lane's eight
+    f16x8_t b[kNB];
   };
-  auto load = [&](lds_u8* st, int kk, Frag& f) {
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      lds_u8* p = st + b_off[nb] + kk * kXRow;
-      const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-      const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * kXRow));
-      f.bh[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-      if constexpr (kXF32) {
-        lds_u8* pl = p + P::kXRegion;
-        const i16x4_t s0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pl);
-        const i16x4_t s1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pl + 4 * kXRow));
-        f.bl[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      lds_u8* p = st + a_off[mb] + kk * kGRow;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f.a[mb][e] = *(lds_f32*)(p + e * kGRow);
+  // Read number k (< kReads) of one k-step's fragments from stage st, in the
+  // order the k-step's matrix instructions use them (row block by row block,
+  // each against every column block): the two transposed reads of g block 0,
+  // the x chunk of every column block, then the g blocks 1, 2, ...
+  constexpr int kReads = kMB * 2 + kNB;  // LDS read instructions per k-step
+  constexpr int kMfma = kMB * kNB;       // matrix instructions per k-step
+  auto read = [&](lds_u8* st, int kk, Frag& f, int k) {
+    if (k < 2 || k >= 2 + kNB) {
+      const int ka = k < 2 ? k : k - kNB;  // index among the 2 kMB g reads
+      const int mb = ka >> 1;
+      lds_u8* p = st + a_off[mb] + kk * 16 * C::kARow + (ka & 1) * 4 * C::kARow;
+      f.a[mb][ka & 1] =
+          __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+    } else {
+      const int nb = k - 2;
+      f.b[nb] = *(lds_f16x8*)(st + b_off[nb] + kk * 2 * C::kBN * 16);
     }
   };
-  auto mma = [&](const Frag& f) {
-    bf16x8_t ah[kMB], al[kMB];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split2(f.a[mb][2 * e], f.a[mb][2 * e + 1], h[e], l[e]);
-      ah[mb] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-      al[mb] = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-    }
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], f.bh[nb], acc[mb][nb], 0, 0, 0);
-    if constexpr (kXF32) {
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], f.bl[nb], acc[mb][nb], 0, 0, 0);
-    }
+  auto mfma = [&](const Frag& f, int k) {
+    const int mb = k / kNB, nb = k % kNB;
+    const f16x8_t a = __builtin_shufflevector(f.a[mb][0], f.a[mb][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, f.b[nb], acc[mb][nb], 0, 0, 0);
+  };
+  auto refill = [&](lds_u8* st, int q, int step) {  // load q (< kLoads) of a stage refill
+    if (q < C::kALoads)
+      load_lds16(g_rsrc, st + (wave * C::kALoads + q) * 1024, a_voff[q] + step * a_step);
+    else
+      load_lds16(x_rsrc, st + C::kARegion + (wave * C::kXLoads + (q - C::kALoads)) * 1024,
+                 x_voff[q - C::kALoads] + step * x_step);
   };
 
-  // Software pipeline over steps of kBT = 32 tokens (two halves of 16).  The
-  // ring holds kS steps; every load is issued unconditionally (steps past the
-  // split read zeros), so the wait counts are the same in every step and the
-  // loop has no branches.  Step s, with the first half's operands already in
-  // registers:
-  //   read the second half of stage s;  matrix work on the first half;
+  // Software pipeline over steps of kBT tokens (kSub k-steps of 16).  The ring
+  // holds kS steps; every load is issued unconditionally (steps past the split
+  // read zeros), so the wait counts are the same in every step and the loop
+  // has no branches.  Step s, with its first k-step's operands in registers:
+  //   k-steps 0 .. kSub-2: matrix work, each instruction followed by its share
+  //   of the reads of the next k-step of stage s;
   //   wait for this wave's loads of step s+1 (kS-2 later steps stay in flight);
   //   barrier: every wave's part of stage s+1 has landed and every wave has
-  //   finished reading stage s;  refill stage s with step s+kS;
-  //   read the first half of stage s+1;  matrix work on the second half.
-  static_assert(kBT == 32, "two halves of 16 tokens per step");
-  static_assert(kS >= 2 && kS <= 4, "ring of 2 to 4 stages");
-  Frag f0, f1;
+  //   finished reading stage s;
+  //   k-step kSub-1: matrix work, each instruction followed by its share of
+  //   the loads refilling stage s with step s+kS and of the reads of the first
+  //   k-step of stage s+1.
+  // sched_barrier keeps this order: the reads are in flight behind independent
+  // matrix work, not issued next to the instruction that consumes them.
+  Frag f[2];
   auto step = [&](int i, int s) {  // i = s % kS, a constant at every call
-    load(stages[i], 16, f1);
-    mma(f0);
-    wait_vmcnt<(kS - 2) * P::kLoadsPerStage>();
+    lds_u8* st = stages[i];
+    lds_u8* nx = stages[(i + 1) % kS];
+#pragma unroll
+    for (int j = 0; j + 1 < C::kSub; ++j) {
+#pragma unroll
+      for (int k = 0; k < kMfma; ++k) {
+        mfma(f[j & 1], k);
+#pragma unroll
+        for (int r = k * kReads / kMfma; r < (k + 1) * kReads / kMfma; ++r)
+          read(st, j + 1, f[(j + 1) & 1], r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_vmcnt<(kS - 2) * C::kLoads>();
     ring_barrier();
-    issue(stages[i], s + kS);
-    load(stages[(i + 1) % kS], 0, f0);
-    mma(f1);
+    constexpr int jl = C::kSub - 1;
+#pragma unroll
+    for (int k = 0; k < kMfma; ++k) {
+      mfma(f[jl & 1], k);
+#pragma unroll
+      for (int q = k * C::kLoads / kMfma; q < (k + 1) * C::kLoads / kMfma; ++q)
+        refill(st, q, s + kS);
+#pragma unroll
+      for (int r = k * kReads / kMfma; r < (k + 1) * kReads / kMfma; ++r)
+        read(nx, 0, f[(jl + 1) & 1], r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  static_assert(C::kSub % 2 == 0, "the fragment buffers alternate, so a step holds an even "
+                "number of k-steps");
 
   issue(stages[0], 0);
   issue(stages[1], 1);
   if constexpr (kS > 2) issue(stages[2], 2);
   if constexpr (kS > 3) issue(stages[3], 3);
-  wait_vmcnt<(kS - 1) * P::kLoadsPerStage>();
+  wait_vmcnt<(kS - 1) * C::kLoads>();
   ring_barrier();
-  load(stages[0], 0, f0);
+#pragma unroll
+  for (int k = 0; k < kReads; ++k) read(stages[0], 0, f[0], k);
   for (int s0 = 0; s0 < nsteps; s0 += kS) {
     step(0, s0);
     step(1, s0 + 1);
@@ -365,64 +383,147 @@ outer_sum_kernel(const float* __restrict__ g, const uint16_t* __restrict__ xh,
 
   // Register r of block (mb, nb) holds row 8*(r/4) + 4*(lane/32) + r%4 and
   // column lane%32 of that 32 x 32 block.
-  float* o = out + split * geo.M * geo.Nd;
+  auto row_of = [&](int mb, int r) {
+    return (int64_t)m0 + wm * kWM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  };
+  auto col_of = [&](int nb) { return (int64_t)n0 + wn * C::kWN + nb * 32 + (lane & 31); };
+
+  float* o = part + split * geo.pstride;
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * kWaveM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = n0 + wn * kWaveN + nb * 32 + (lane & 31);
-        if (m < geo.M && n < geo.Nd) o[m * geo.Nd + n] = acc[mb][nb][r];
+        const int64_t m = row_of(mb, r), n = col_of(nb);
+        if (m < geo.M && n < d) o[m * d + n] = acc[mb][nb][r];
       }
-}
 
-// G[e] = sum_s part[s][e] in split order (four elements per thread).
-__global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ part,
-                                                           int64_t nsplit, int64_t n,
-                                                           float* __restrict__ G) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t n4 = n / 4;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4; e += stride) {
-    float4 s = reinterpret_cast<const float4*>(part)[e];
-    for (int64_t q = 1; q < nsplit; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(part + q * n)[e];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  // One workgroup per split lists the split's tokens left out of the fp16
+  // operands, in token order, for the exact fp32 pass of finish_kernel.  Its
+  // first flag words were loaded before the main loop (fbits); a split with
+  // no flag set (the usual case) only writes its count.
+  if (lister) {
+    for (int64_t i = ((int64_t)kEarlyWords * C::kThreads + tid) * 4; i < t_rows;
+         i += (int64_t)C::kThreads * 4)
+      fbits |= flag_word(i);
+    if (!__syncthreads_or(fbits != 0u)) {
+      if (tid == 0) count[split] = 0;
+      return;
     }
-    reinterpret_cast<float4*>(G)[e] = s;
   }
-  for (int64_t e = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
-    float s = part[e];
-    for (int64_t q = 1; q < nsplit; ++q) s += part[q * n + e];
-    G[e] = s;
+  if (lister) {
+    __shared__ int wsum[C::kWaves];
+    int base = 0;
+    for (int64_t c0 = 0; c0 < t_rows; c0 += C::kThreads) {
+      const int64_t i = c0 + tid;
+      const int fl = (i < t_rows) ? flags[t_begin + i] : 0;
+      const uint64_t bal = __ballot(fl);
+      if (lane == 0) wsum[wave] = __popcll(bal);
+      __syncthreads();
+      int off = base, all = 0;
+      for (int w = 0; w < C::kWaves; ++w) {
+        off += w < wave ? wsum[w] : 0;
+        all += wsum[w];
+      }
+      if (fl) list[t_begin + off + __popcll(bal & ((1ull << lane) - 1ull))] = (int32_t)(t_begin + i);
+      base += all;
+      __syncthreads();
+    }
+    if (tid == 0) count[split] = base;
   }
 }
 
-template <bool kXF32>
-static GemmGeom plan_t(int64_t T, int64_t M, int64_t Nd) {
-  using P = Pipe<kXF32>;
-  GemmGeom g;
+// G[e] = sum_s part[s][e] in split order, then plus g[t][m] x[t][n] in fp32 for
+// each token the fp16 operands left out (split by split, in token order).
+// Four elements per thread.
+__global__ void __launch_bounds__(256) finish_kernel(const float* __restrict__ part,
+                                                     int64_t nsplit, int64_t pstride, int64_t M,
+                                                     int64_t d, const int32_t* __restrict__ list,
+                                                     const int32_t* __restrict__ count,
+                                                     int64_t t_per_split,
+                                                     const float* __restrict__ g32,
+                                                     const void* __restrict__ X, int x_bf16,
+                                                     float* __restrict__ G) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  for (int64_t q = threadIdx.x; q < nsplit; q += 256)
+    if (count[q] != 0) any = 1;
+  __syncthreads();
+  const int64_t n = M * d;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * e4 < n; e4 += stride) {
+    const int64_t e = 4 * e4;
+    float v[4];
+    if (e + 4 <= n) {
+      // split order; four partials loaded at a time so that their reads overlap
+      float4 s = reinterpret_cast<const float4*>(part)[e4];
+      int64_t q = 1;
+      for (; q + 4 <= nsplit; q += 4) {
+        float4 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = reinterpret_cast<const float4*>(part + (q + u) * pstride)[e4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s.x += w[u].x; s.y += w[u].y; s.z += w[u].z; s.w += w[u].w;
+        }
+      }
+      for (; q < nsplit; ++q) {
+        const float4 w = reinterpret_cast<const float4*>(part + q * pstride)[e4];
+        s.x += w.x; s.y += w.y; s.z += w.z; s.w += w.w;
+      }
+      v[0] = s.x; v[1] = s.y; v[2] = s.z; v[3] = s.w;
+    } else {
+      for (int k = 0; k < 4; ++k) {
+        v[k] = 0.f;
+        if (e + k < n)
+          for (int64_t q = 0; q < nsplit; ++q) v[k] += part[q * pstride + e + k];
+      }
+    }
+    if (any) {
+      for (int k = 0; k < 4 && e + k < n; ++k) {
+        const int64_t m = (e + k) / d, c = (e + k) % d;
+        for (int64_t q = 0; q < nsplit; ++q) {
+          const int32_t* lq = list + q * t_per_split;
+          for (int i = 0; i < count[q]; ++i) {
+            const int64_t t = lq[i];
+            v[k] = fmaf(g32[t * M + m], load_x(X, x_bf16, t * d + c), v[k]);
+          }
+        }
+      }
+    }
+    if (e + 4 <= n) {
+      reinterpret_cast<float4*>(G)[e4] = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int k = 0; k < 4 && e + k < n; ++k) G[e + k] = v[k];
+    }
+  }
+}
+
+static Gemm16Geom plan16(int64_t T, int64_t M, int64_t d) {
+  using C = GemmCfg;
+  Gemm16Geom g;
   g.M = M;
-  g.Mp = (M + 3) / 4 * 4;
-  g.Nd = Nd;
-  g.dp = (Nd + 7) / 8 * 8;
+  g.Mp = (M + 7) / 8 * 8;
+  g.d = d;
   g.T = T;
-  g.tiles_m = (M + kBM - 1) / kBM;
-  g.tiles_n = (Nd + kBN - 1) / kBN;
+  g.tiles_m = (M + C::kBM - 1) / C::kBM;
+  g.tiles_n = (d + C::kBN - 1) / C::kBN;
   const int64_t tiles = g.tiles_m * g.tiles_n;
   // One wave of workgroups over the 256 CUs, with >= 1024 tokens per split.
-  const int64_t slots = 256 * P::kWgPerCu;
-  int64_t want = (slots + tiles - 1) / tiles;
+  int64_t want = (256 + tiles - 1) / tiles;
   int64_t cap = (T + 1023) / 1024;
   if (cap < 1) cap = 1;
   int64_t ns = want < cap ? want : cap;
   if (ns < 1) ns = 1;
   int64_t per = (T + ns - 1) / ns;
-  constexpr int64_t gran = P::kS * P::kBT;  // whole ring turns per split
+  constexpr int64_t gran = C::kS * C::kBT;  // whole ring turns per split
   per = (per + gran - 1) / gran * gran;
-  // 32-bit buffer offsets: one split's rows of g (and of X) stay below 2^31 bytes.
-  const int64_t row_bytes = 4 * (g.Mp + kBM) > 2 * (g.dp + kBN) ? 4 * (g.Mp + kBM) : 2 * (g.dp + kBN);
+  // 32-bit buffer offsets: a split's rows of g16 (and token groups of x16),
+  // plus one ring turn of prefetch past them, stay below 2^31 bytes.
+  const int64_t rb_g = 2 * (g.Mp + C::kBM), rb_x = 2 * (d + C::kBN);
+  const int64_t row_bytes = rb_g > rb_x ? rb_g : rb_x;
   const int64_t per_max = ((((int64_t)1 << 31) - 1) / row_bytes - 3 * gran) / gran * gran;
   if (per > per_max) per = per_max > gran ? per_max : gran;
   g.t_per_split = per > 0 ? per : gran;
@@ -430,88 +531,86 @@ static GemmGeom plan_t(int64_t T, int64_t M, int64_t Nd) {
   if (g.nsplit < 1) g.nsplit = 1;
   g.groups = g.tiles_m * g.nsplit;
   g.groups_per_xcd = (g.groups + kXcds - 1) / kXcds;
+  g.pstride = (M * d + 63) / 64 * 64;
   return g;
 }
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Workspace: X planes [T][dp] bf16 (hi, lo; used for fp32 X or d % 8 != 0),
-// padded g [T][Np] (N % 4 != 0 only), split partials [S][N][d] fp32.
+// Workspace: g16 [T][Mp], x16 [ceil(T/8)][d][8], flags [T], the per-split
+// lists of left-out tokens [T] int32 and their counts [S], the split partials
+// [S][pstride] fp32.
 struct WsLayout {
-  size_t plane, gpad, part;
+  size_t g16, x16, flags, list, count, part;
+  size_t total() const { return g16 + x16 + flags + list + count + part; }
 };
 static WsLayout ws_layout(int64_t T, int64_t N, int64_t d) {
-  const GemmGeom a = plan_t<false>(T, N, d), b = plan_t<true>(T, N, d);
-  const int64_t ns = a.nsplit > b.nsplit ? a.nsplit : b.nsplit;
+  const Gemm16Geom a = plan16(T, N, d);
   WsLayout w;
-  w.plane = align256((size_t)T * (size_t)a.dp * 2);
-  w.gpad = N % 4 ? align256((size_t)T * (size_t)a.Mp * 4) : 0;
-  w.part = ns > 1 ? (size_t)ns * (size_t)N * (size_t)d * sizeof(float) : 0;
+  w.g16 = align256((size_t)T * (size_t)a.Mp * 2);
+  w.x16 = align256((size_t)((T + 7) / 8) * (size_t)d * 16);
+  w.flags = align256((size_t)T);
+  w.list = align256((size_t)T * 4);
+  w.count = align256((size_t)a.nsplit * 4);
+  w.part = (size_t)a.nsplit * (size_t)a.pstride * sizeof(float);
   return w;
 }
 
 bool outer_sum_supported(int64_t T, int64_t N, int64_t d) {
   // one workgroup per (tile, split): the grid's work-items must fit 32 bits
-  const GemmGeom a = plan_t<false>(T, N, d), b = plan_t<true>(T, N, d);
-  const int64_t na = a.groups_per_xcd * kXcds * a.tiles_n;
-  const int64_t nb = b.groups_per_xcd * kXcds * b.tiles_n;
-  return (na > nb ? na : nb) < ((int64_t)1 << 24);
+  const Gemm16Geom a = plan16(T, N, d);
+  return a.groups_per_xcd * kXcds * a.tiles_n < ((int64_t)1 << 24);
 }
 
 size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d) {
-  const WsLayout w = ws_layout(T, N, d);
-  return 2 * w.plane + w.gpad + w.part;
+  return ws_layout(T, N, d).total();
 }
 
-template <bool kXF32>
-static hipError_t launch_gemm_t(const GemmGeom& geo, const float* g, const uint16_t* xh,
-                                const uint16_t* xl, float* out, hipStream_t s) {
+Gemm16Out outer_sum_operands(void* workspace, int64_t T, int64_t N, int64_t d, const void* X,
+                             bool x_bf16) {
+  const WsLayout w = ws_layout(T, N, d);
+  char* ws = reinterpret_cast<char*>(workspace);
+  Gemm16Out o;
+  o.g16 = reinterpret_cast<uint16_t*>(ws);
+  o.x16 = reinterpret_cast<uint16_t*>(ws + w.g16);
+  o.flags = reinterpret_cast<uint8_t*>(ws + w.g16 + w.x16);
+  o.X = X;
+  o.T = T;
+  o.Mp = (N + 7) / 8 * 8;
+  o.d = d;
+  o.x_bf16 = x_bf16 ? 1 : 0;
+  return o;
+}
+
+hipError_t launch_outer_sum16(const Gemm16Out& o, const float* g32, int64_t N, float* G,
+                              void* workspace, hipStream_t s) {
+  const Gemm16Geom geo = plan16(o.T, N, o.d);
+  const WsLayout w = ws_layout(o.T, N, o.d);
+  char* ws = reinterpret_cast<char*>(workspace) + w.g16 + w.x16 + w.flags;
+  int32_t* list = reinterpret_cast<int32_t*>(ws);
+  int32_t* count = reinterpret_cast<int32_t*>(ws + w.list);
+  float* part = reinterpret_cast<float*>(ws + w.list + w.count);
   const int64_t nwg = geo.groups_per_xcd * kXcds * geo.tiles_n;
-  hipLaunchKernelGGL(outer_sum_kernel<kXF32>, dim3((uint32_t)nwg), dim3(256), 0, s, g, xh, xl, geo,
-                     out);
+  hipLaunchKernelGGL(gemm16_kernel<GemmCfg>, dim3((uint32_t)nwg), dim3(GemmCfg::kThreads), 0, s,
+                     o.g16, o.x16, o.flags, geo, part, list, count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = N * o.d;
+  int64_t blocks = ((n + 3) / 4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(finish_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, part, geo.nsplit,
+                     geo.pstride, N, o.d, list, count, geo.t_per_split, g32, o.X, o.x_bf16, G);
   return hipGetLastError();
 }
 
 hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
                             int64_t d, float* G, void* workspace, hipStream_t s) {
-  const GemmGeom geo = x_bf16 ? plan_t<false>(T, N, d) : plan_t<true>(T, N, d);
-  const WsLayout w = ws_layout(T, N, d);
-  char* ws = reinterpret_cast<char*>(workspace);
-  uint16_t* ph = reinterpret_cast<uint16_t*>(ws);
-  uint16_t* pl = reinterpret_cast<uint16_t*>(ws + w.plane);
-  float* gpad = reinterpret_cast<float*>(ws + 2 * w.plane);
-  float* part = reinterpret_cast<float*>(ws + 2 * w.plane + w.gpad);
-  float* out = (geo.nsplit > 1) ? part : G;
-
-  const uint16_t* xh = reinterpret_cast<const uint16_t*>(X);
-  if (!x_bf16 || d % 8 != 0) {
-    const int64_t n = T * (geo.dp / 8);
-    const dim3 grid((uint32_t)(n / 256 < 16384 ? n / 256 + 1 : 16384));
-    if (x_bf16)
-      hipLaunchKernelGGL(x_planes_kernel<false>, grid, dim3(256), 0, s, X, T, d, geo.dp, ph, nullptr);
-    else
-      hipLaunchKernelGGL(x_planes_kernel<true>, grid, dim3(256), 0, s, X, T, d, geo.dp, ph, pl);
-    xh = ph;
-  }
-  const float* gg = g;
-  if (N % 4 != 0) {
-    int64_t blocks = (T * geo.Mp + 255) / 256;
-    if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(g_pad_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, g, T, N, geo.Mp, gpad);
-    gg = gpad;
-  }
-  hipError_t e = hipGetLastError();
+  const Gemm16Out o = outer_sum_operands(workspace, T, N, d, X, x_bf16);
+  hipLaunchKernelGGL(prep16_kernel, dim3((uint32_t)T), dim3(256), 0, s, g, N, o);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = x_bf16 ? launch_gemm_t<false>(geo, gg, xh, nullptr, out, s)
-             : launch_gemm_t<true>(geo, gg, ph, pl, out, s);
-  if (e != hipSuccess || geo.nsplit <= 1) return e;
-  const int64_t n = N * d;
-  int64_t blocks = (n / 4 + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, part,
-                     geo.nsplit, n, G);
-  return hipGetLastError();
+  return launch_outer_sum16(o, g, N, G, workspace, s);
 }
 
 }  // namespace dust

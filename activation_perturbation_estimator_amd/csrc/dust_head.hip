@@ -30,6 +30,7 @@
 //                   writes g_t = (sum delta a - dbar sum a) / (K sigma) once.
 //                   The noise is generated exactly once per (draw, token, column).
 #include "dust_device.hpp"
+#include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
 
 namespace dust {
@@ -121,10 +122,12 @@ template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds, int kDraws>
 __global__ void __launch_bounds__(64 * kW)
 head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, int64_t T,
             int64_t V, float sigma, int64_t K, uint32_t stream, uint32_t k0, uint32_t k1,
-            float* __restrict__ g_hat, float* __restrict__ losses, float* __restrict__ delta_out) {
+            float* __restrict__ g_hat, float* __restrict__ losses, float* __restrict__ delta_out,
+            Gemm16Out op) {
   constexpr int kCols = 4 * kNB;
   extern __shared__ float smem[];
-  float* red = smem;             // reductions: 2 kW + 2 kDraws kW <= 128 floats
+  float* red = smem;             // reductions: 2 kW + 2 kDraws kW <= 64 floats, then
+                                 // 3 kW <= 48 at smem + 64 for the G_W operands
   float* zs = smem + 128;        // kNB * 64 * kW * 4 floats when kZInLds
 
   const int lane = threadIdx.x & 63;
@@ -277,18 +280,18 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
     const float dbar = sum_delta / (float)K;
     const float scale = kBoxMullerScale / ((float)K * sigma);
     float* grow = g_hat + t * V;
+    float gv[kCols];
+#pragma unroll
+    for (int q = 0; q < kCols; ++q) gv[q] = (acc_da[q] - dbar * acc_a[q]) * scale;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const int64_t j = (int64_t)b * 64 * kW + wave * 64 + lane;
-      if (j < nblk) {
-        float4 o;
-        o.x = (acc_da[4 * b] - dbar * acc_a[4 * b]) * scale;
-        o.y = (acc_da[4 * b + 1] - dbar * acc_a[4 * b + 1]) * scale;
-        o.z = (acc_da[4 * b + 2] - dbar * acc_a[4 * b + 2]) * scale;
-        o.w = (acc_da[4 * b + 3] - dbar * acc_a[4 * b + 3]) * scale;
-        *reinterpret_cast<float4*>(grow + 4 * j) = o;
-      }
+      if (j < nblk)
+        *reinterpret_cast<float4*>(grow + 4 * j) =
+            make_float4(gv[4 * b], gv[4 * b + 1], gv[4 * b + 2], gv[4 * b + 3]);
     }
+    // The fp16 operands of the G_W pass: this workgroup owns the token's whole row.
+    if (op.g16 != nullptr) emit_operands<kNB, kW>(op, t, V, gv, smem + 64);
   }
 }
 
@@ -341,7 +344,8 @@ bool head_fused_supported(int64_t V) { return fused_shape(V).nb != 0; }
 template <int kNB, int kW, bool kFused, typename ZT, bool kZInLds>
 static hipError_t launch_head_t(const void* logits, const int32_t* targets, int64_t T, int64_t V,
                                 float sigma, int64_t K, uint32_t stream, uint64_t seed,
-                                float* g_hat, float* losses, float* delta, hipStream_t s) {
+                                float* g_hat, float* losses, float* delta, const Gemm16Out& op,
+                                hipStream_t s) {
   constexpr int kDraws = kFused ? fused_draws(kNB) : 1;
   const size_t lds = sizeof(float) * (128 + (kZInLds ? (size_t)kNB * 64 * kW * 4 : 0));
   if (lds > 65536) {  // above the default dynamic-LDS limit: raise it for this kernel
@@ -353,7 +357,7 @@ static hipError_t launch_head_t(const void* logits, const int32_t* targets, int6
   hipLaunchKernelGGL((head_kernel<kNB, kW, kFused, ZT, kZInLds, kDraws>), dim3((uint32_t)T),
                      dim3(64 * kW),
                      lds, s, reinterpret_cast<const ZT*>(logits), targets, T, V, sigma, K, stream,
-                     (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, losses, delta);
+                     (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, losses, delta, op);
   return hipGetLastError();
 }
 
@@ -361,13 +365,13 @@ template <bool kFused, typename ZT>
 static hipError_t launch_head_dispatch(const void* logits, const int32_t* targets, int64_t T,
                                        int64_t V, float sigma, int64_t K, uint32_t stream,
                                        uint64_t seed, float* g_hat, float* losses, float* delta,
-                                       hipStream_t s) {
+                                       const Gemm16Out& op, hipStream_t s) {
   const HeadShape h = kFused ? fused_shape(V) : wide_shape(V);
   const bool lds = V <= kLdsVocabMax;
 #define DUST_HEAD_CASE(NB, W, LDS)                                                              \
   if (h.nb == NB && h.w == W && lds == LDS)                                                     \
     return launch_head_t<NB, W, kFused, ZT, LDS>(logits, targets, T, V, sigma, K, stream, seed, \
-                                                 g_hat, losses, delta, s);
+                                                 g_hat, losses, delta, op, s);
   DUST_HEAD_CASE(1, 1, true)
   DUST_HEAD_CASE(2, 1, true)
   DUST_HEAD_CASE(4, 1, true)
@@ -391,24 +395,26 @@ static hipError_t launch_head_dispatch(const void* logits, const int32_t* target
 
 hipError_t launch_head_fused(const void* logits, bool logits_bf16, const int32_t* targets,
                              int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
-                             uint64_t seed, float* g_hat, float* losses, hipStream_t s) {
+                             uint64_t seed, float* g_hat, float* losses, const Gemm16Out& op,
+                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   return logits_bf16
              ? launch_head_dispatch<true, uint16_t>(logits, targets, T, V, sigma, K, stream, seed,
-                                                    g_hat, losses, nullptr, s)
+                                                    g_hat, losses, nullptr, op, s)
              : launch_head_dispatch<true, float>(logits, targets, T, V, sigma, K, stream, seed,
-                                                 g_hat, losses, nullptr, s);
+                                                 g_hat, losses, nullptr, op, s);
 }
 
 hipError_t launch_head_losses(const void* logits, bool logits_bf16, const int32_t* targets,
                               int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
                               uint64_t seed, float* losses, float* delta, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  Gemm16Out none{};
   return logits_bf16
              ? launch_head_dispatch<false, uint16_t>(logits, targets, T, V, sigma, K, stream, seed,
-                                                     nullptr, losses, delta, s)
+                                                     nullptr, losses, delta, none, s)
              : launch_head_dispatch<false, float>(logits, targets, T, V, sigma, K, stream, seed,
-                                                  nullptr, losses, delta, s);
+                                                  nullptr, losses, delta, none, s);
 }
 
 }  // namespace dust

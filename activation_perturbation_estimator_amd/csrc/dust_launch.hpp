@@ -15,6 +15,17 @@ hipError_t launch_philox_raw(const uint32_t* ctr, uint32_t* out, int64_t n, uint
 hipError_t launch_noise_fill(float* out, int64_t ndraw, int64_t T, int64_t N, uint32_t draw0,
                              uint32_t stream, uint64_t seed, hipStream_t s);
 
+// Where a kernel that produces g writes the fp16 operands of the G_W pass
+// (layout and scale rule in dust_gemm16.hpp); g16 == nullptr: not wanted.
+struct Gemm16Out {
+  uint16_t* g16;   // [T][Mp]
+  uint16_t* x16;   // [ceil(T/8)][d][8]
+  uint8_t* flags;  // [T]
+  const void* X;   // [T][d] layer input, bf16 (x_bf16) or fp32
+  int64_t T, Mp, d;
+  int x_bf16;
+};
+
 // LM head.  Work split: one workgroup of 64*w threads per token, nb Philox
 // blocks per lane per draw.
 struct HeadShape {
@@ -26,7 +37,8 @@ HeadShape wide_shape(int64_t V);    // per-draw losses and the error estimate
 bool head_fused_supported(int64_t V);
 hipError_t launch_head_fused(const void* logits, bool logits_bf16, const int32_t* targets,
                              int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
-                             uint64_t seed, float* g_hat, float* losses, hipStream_t s);
+                             uint64_t seed, float* g_hat, float* losses, const Gemm16Out& op,
+                             hipStream_t s);
 hipError_t launch_head_losses(const void* logits, bool logits_bf16, const int32_t* targets,
                               int64_t T, int64_t V, float sigma, int64_t K, uint32_t stream,
                               uint64_t seed, float* losses, float* delta, hipStream_t s);
@@ -38,11 +50,18 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
 
 // Error estimate from rewards with regenerated noise.
 hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
-                                 uint32_t stream, uint64_t seed, float* g_hat, hipStream_t s);
+                                 uint32_t stream, uint64_t seed, float* g_hat,
+                                 const Gemm16Out& op, hipStream_t s);
 
-// Outer-product sum G = g^T X on the matrix cores.
+// Outer-product sum G = g^T X on the matrix cores.  The workspace starts with
+// the fp16 operands (outer_sum_operands), written either by the kernel that
+// produced g or, for a caller's g, by launch_outer_sum's own pass.
 size_t outer_sum_workspace_bytes(int64_t T, int64_t N, int64_t d);
 bool outer_sum_supported(int64_t T, int64_t N, int64_t d);  // the launch grid fits
+Gemm16Out outer_sum_operands(void* workspace, int64_t T, int64_t N, int64_t d, const void* X,
+                             bool x_bf16);
+hipError_t launch_outer_sum16(const Gemm16Out& op, const float* g32, int64_t N, float* G,
+                              void* workspace, hipStream_t s);
 hipError_t launch_outer_sum(const float* g, const void* X, bool x_bf16, int64_t T, int64_t N,
                             int64_t d, float* G, void* workspace, hipStream_t s);
 

@@ -16,8 +16,9 @@ namespace dust {
 // c[i,t] = mean_j x[j,t] - x[i,t].  One thread per token; the mean is summed in
 // fp64 over the draws (fixed order), so the result does not depend on K's size
 // beyond fp32 rounding of the output.  Memory-bound: 12 bytes per element.
-__global__ void __launch_bounds__(256) centre_kernel(const float* __restrict__ x, int64_t K,
-                                                     int64_t T, float* __restrict__ c) {
+// c may be x (the estimator centres in place), so neither pointer is restrict.
+__global__ void __launch_bounds__(256) centre_kernel(const float* x, int64_t K, int64_t T,
+                                                     float* c) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   double s = 0.0;
@@ -33,10 +34,10 @@ __global__ void __launch_bounds__(256) centre_kernel(const float* __restrict__ x
 // scan of each lane's kE elements with zero carry, a wave-wide suffix scan of
 // the lanes' affine maps x -> A + B x (B = gamma^kE), and a second serial pass
 // with the true carry.
+// r may be c (the estimator scans in place), so neither pointer is restrict.
 template <int kE>
-__global__ void __launch_bounds__(256) reward_scan_kernel(const float* __restrict__ c, int64_t K,
-                                                          int64_t T, int64_t L, float gamma,
-                                                          float* __restrict__ r) {
+__global__ void __launch_bounds__(256) reward_scan_kernel(const float* c, int64_t K, int64_t T,
+                                                          int64_t L, float gamma, float* r) {
   constexpr int kTile = 64 * kE;
   __shared__ float buf[4][64 * (kE + 1)];  // rows of kE + 1: conflict-free lane-major reads
   const int lane = threadIdx.x & 63;

@@ -54,6 +54,40 @@ __global__ void __launch_bounds__(256) mfma_only(float* out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// 1b. The same for fp16 (v_mfma_f32_32x32x16_f16) or bf16 operands, with kBlocks
+// independent accumulator blocks (16: 256 accumulator registers per lane, as
+// a 128 x 128 wave tile) used round-robin, 32 MFMAs per iteration.
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+template <bool kF16, int kBlocks>
+__global__ void __launch_bounds__(256, 1) mfma_rate(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  f16x8_t ah[4], bh[4];
+  bf16x8_t ab[4], bb[4];
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) {
+      ah[j][i] = (_Float16)(lane * 0.01f + i + j);
+      bh[j][i] = (_Float16)(0.25f * j + i * 0.125f);
+      ab[j][i] = (__bf16)(lane * 0.01f + i + j);
+      bb[j][i] = (__bf16)(0.25f * j + i * 0.125f);
+    }
+  f32x16_t acc[kBlocks];
+  for (int x = 0; x < kBlocks; ++x)
+    for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int x = k % kBlocks;
+      if constexpr (kF16)
+        acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[k & 3], bh[(k >> 2) & 3], acc[x], 0, 0, 0);
+      else
+        acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[k & 3], bb[(k >> 2) & 3], acc[x], 0, 0, 0);
+    }
+  float s = 0.f;
+  for (int x = 0; x < kBlocks; ++x)
+    for (int r = 0; r < 16; ++r) s += acc[x][r];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 // 2. LDS reads: 8 reads per iteration of one form, addresses moving with the
 // iteration (so that nothing is hoisted), summed into a register.
 //   kForm 0 ds_read_b32, 1 ds_read_b64, 2 ds_read_b128, 3 ds_read_b64_tr_b16
@@ -220,6 +254,24 @@ int main() {
     const double fl = mfma_flops * 16.0 * iters * wgs * 4;
     printf("  %d wave(s)/SIMD  %.3f ms  %7.1f TFLOP/s  (%.2f GHz at 32 cycles per MFMA)\n",
            wgs / 256, ms, fl / ms / 1e9, 16.0 * iters * wgs * 4 / 1024 * 32 / (ms * 1e-3) / 1e9);
+  }
+
+  printf("MFMA 32x32x16 rate by operand type and accumulator blocks (32 per iteration, 1 wave/SIMD):\n");
+  {
+    const int iters = 2048, wgs = 256;
+    const char* nm[4] = {"bf16,  8 blocks", "bf16, 16 blocks", "fp16,  8 blocks", "fp16, 16 blocks"};
+    for (int v = 0; v < 4; ++v) {
+      float ms = 0.f;
+      switch (v) {
+        case 0: ms = time_ms([](float* o, int g, int it) { hipLaunchKernelGGL((mfma_rate<false, 8>), dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters); break;
+        case 1: ms = time_ms([](float* o, int g, int it) { hipLaunchKernelGGL((mfma_rate<false, 16>), dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters); break;
+        case 2: ms = time_ms([](float* o, int g, int it) { hipLaunchKernelGGL((mfma_rate<true, 8>), dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters); break;
+        default: ms = time_ms([](float* o, int g, int it) { hipLaunchKernelGGL((mfma_rate<true, 16>), dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters); break;
+      }
+      const double fl = mfma_flops * 32.0 * iters * wgs * 4;
+      printf("  %s  %.3f ms  %7.1f TFLOP/s  (%.2f GHz at 32 cycles per MFMA)\n", nm[v], ms,
+             fl / ms / 1e9, 32.0 * iters * wgs * 4 / 1024 * 32 / (ms * 1e-3) / 1e9);
+    }
   }
 
   printf("LDS reads, bytes per clock per CU at 2.1 GHz (512 / 1024 workgroups of 256):\n");

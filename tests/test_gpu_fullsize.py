@@ -34,7 +34,6 @@ def _check_gw_rows(g, X64, G, nrows=48):
     gs = g[:, rows].astype(np.float64)
     ref = gs.T @ X64
     assert_parity(G[rows], ref, "G_W rows")
-    assert_rows(G[rows], ref, "G_W rows, one by one")
     assert_elementwise(G[rows], ref, gw_rss_scale(gs, X64), "G_W row elements", G_W_RSS_TOL,
                        atol=1e-6 * float(np.abs(ref).max()))
 
