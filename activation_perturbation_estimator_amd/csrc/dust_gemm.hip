@@ -400,8 +400,8 @@ gemm16_kernel(const uint16_t* __restrict__ g16, const uint16_t* __restrict__ x16
       }
 
   // One workgroup per split lists the split's tokens left out of the fp16
-  // operands, in token order, for the exact fp32 pass of finish_kernel.  Its
-  // first flag words were loaded before the main loop (fbits); a split with
+  // operands, in token order, for the exact fp32 pass of split_finish_kernel.
+  // Its first flag words were loaded before the main loop (fbits); a split with
   // no flag set (the usual case) only writes its count.
   if (lister) {
     for (int64_t i = ((int64_t)kEarlyWords * C::kThreads + tid) * 4; i < t_rows;
@@ -437,7 +437,7 @@ gemm16_kernel(const uint16_t* __restrict__ g16, const uint16_t* __restrict__ x16
 // G[e] = sum_s part[s][e] in split order, then plus g[t][m] x[t][n] in fp32 for
 // each token the fp16 operands left out (split by split, in token order).
 // Four elements per thread.
-__global__ void __launch_bounds__(256) finish_kernel(const float* __restrict__ part,
+__global__ void __launch_bounds__(256) split_finish_kernel(const float* __restrict__ part,
                                                      int64_t nsplit, int64_t pstride, int64_t M,
                                                      int64_t d, const int32_t* __restrict__ list,
                                                      const int32_t* __restrict__ count,
@@ -599,7 +599,7 @@ hipError_t launch_outer_sum16(const Gemm16Out& o, const float* g32, int64_t N, f
   int64_t blocks = ((n + 3) / 4 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(finish_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, part, geo.nsplit,
+  hipLaunchKernelGGL(split_finish_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, part, geo.nsplit,
                      geo.pstride, N, o.d, list, count, geo.t_per_split, g32, o.X, o.x_bf16, G);
   return hipGetLastError();
 }
