@@ -20,16 +20,16 @@ from __future__ import annotations
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import (DUST_BF16, DUST_F32, DUST_N_MAX, DUST_SIGMA_MAX, DUST_STAGE_EVENTS,
-                   DustError)
+from ._lib import (DUST_BF16, DUST_EMBEDDING_NOALLOC_BYTES, DUST_F32, DUST_N_MAX, DUST_SIGMA_MAX,
+                   DUST_STAGE_EVENTS, DustError)
 
 __all__ = [
     "head_estimate", "linear_estimate", "noise", "philox4x32_10", "head_losses", "centre",
     "reward_scan", "error_estimate", "outer_sum", "perturbed_linear", "embedding_grad",
-    "sgd_momentum_", "adam_", "ce_grad", "check_targets",
+    "embedding_grad_noalloc", "sgd_momentum_", "adam_", "ce_grad", "check_targets",
     "head_workspace_size",
     "linear_workspace_size", "outer_sum_workspace_size", "version", "DustError",
-    "DUST_SIGMA_MAX", "DUST_N_MAX", "DUST_STAGE_EVENTS",
+    "DUST_SIGMA_MAX", "DUST_N_MAX", "DUST_STAGE_EVENTS", "DUST_EMBEDDING_NOALLOC_BYTES",
 ]
 
 
@@ -307,6 +307,22 @@ def embedding_grad(ids, g_hat, vocab: int, out=None, workspace=None):
                                  _dev(G, "G_E"), ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream(g_hat.device))
     _lib.check("dust_embedding_grad", st)
+    return G
+
+
+def embedding_grad_noalloc(ids, g_hat, vocab: int, out=None):
+    """embedding_grad without a workspace: the library's own fixed scratch
+    (DUST_EMBEDDING_NOALLOC_BYTES per GPU), for callers that cannot allocate
+    device memory.  ``out`` should be preallocated by such a caller."""
+    torch = _torch()
+    T, N = g_hat.shape
+    _expect(g_hat, "g_hat", dtypes=_f32())
+    _expect(ids, "ids", (T,), torch.int32, g_hat.device)
+    (G,) = _outputs(out, [(int(vocab), N)], g_hat.device, ["out"])
+    st = _lib.load().dust_embedding_grad_noalloc(_dev(ids, "ids"), _dev(g_hat, "g_hat"), T, N,
+                                                 int(vocab), _dev(G, "G_E"),
+                                                 _stream(g_hat.device))
+    _lib.check("dust_embedding_grad_noalloc", st)
     return G
 
 

@@ -24,6 +24,7 @@ DUST_BF16 = 1
 DUST_SIGMA_MAX = 8.0
 DUST_N_MAX = 65536
 DUST_STAGE_EVENTS = 4
+DUST_EMBEDDING_NOALLOC_BYTES = 16 << 20
 
 _i64 = ctypes.c_int64
 _u64 = ctypes.c_uint64
@@ -55,6 +56,8 @@ SIGNATURES = {
                                      _i64, _vp, _vp]),
     "dust_embedding_grad": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "dust_embedding_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "dust_embedding_grad_noalloc": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "dust_embedding_noalloc_bytes": (_sz, [_i64, _i64, _i64]),
     "dust_sgd_momentum": (_int, [_vp, _vp, _vp, _i64, _f32, _f32, _f32, _vp]),
     "dust_adam": (_int, [_vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "dust_ce_grad": (_int, [_vp, _int, _vp, _i64, _i64, _vp, _vp]),

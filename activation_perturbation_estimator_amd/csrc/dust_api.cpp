@@ -11,6 +11,9 @@
 #include "dust.h"
 #include "dust_launch.hpp"
 
+static_assert(DUST_EMBEDDING_NOALLOC_BYTES == dust::kEmbeddingStaticScratchBytes,
+              "the header states the size of the library's own scratch");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -311,6 +314,27 @@ dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t 
     return DUST_ERR_WORKSPACE;
   return hip_status(dust::launch_embedding_grad(ids, g_hat, T, N, vocab, G_E,
                                                 aligned_base(workspace), as_stream(s)));
+}
+
+dust_status dust_embedding_grad_noalloc(const int32_t* ids, const float* g_hat, int64_t T,
+                                        int64_t N, int64_t vocab, float* G_E, dust_stream_t s) {
+  if (!ids || !g_hat || !G_E || T < 0 || N <= 0 || N % 4 != 0 || vocab <= 0)
+    return DUST_ERR_INVALID_ARG;
+  if (T > kMaxT || N > kMaxWidth || vocab > ((int64_t)1 << 24) || T * N > kMaxElems ||
+      vocab * N > kMaxElems)
+    return DUST_ERR_UNSUPPORTED;
+  if (((T + 511) / 512) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
+  if (dust::embedding_workspace_bytes(T, N, vocab) > DUST_EMBEDDING_NOALLOC_BYTES)
+    return DUST_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (dust::embedding_static_scratch(&scratch) != hipSuccess) return DUST_ERR_HIP;
+  return hip_status(dust::launch_embedding_grad(ids, g_hat, T, N, vocab, G_E, scratch,
+                                                as_stream(s)));
+}
+
+size_t dust_embedding_noalloc_bytes(int64_t T, int64_t N, int64_t vocab) {
+  if (T < 0 || N <= 0 || vocab <= 0) return 0;
+  return dust::embedding_workspace_bytes(T, N, vocab);
 }
 
 dust_status dust_sgd_momentum(float* W, const float* G, float* m, int64_t n, float lr,

@@ -26,6 +26,8 @@
 //   6. finish_kernel   : per id, the zero row of an absent id, or the in-order
 //                        sum of the partials of an id that spans segments.
 // Ids outside [0, vocab) are skipped.
+#include <mutex>
+
 #include "dust_device.hpp"
 #include "dust_launch.hpp"
 
@@ -351,6 +353,36 @@ hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, 
   const int64_t fb = vocab < 65536 ? vocab : 65536;
   hipLaunchKernelGGL(finish_kernel, dim3((uint32_t)fb), dim3(128), 0, s, N, start, vocab, part, GE);
   return hipGetLastError();
+}
+
+// Scratch memory of the variant that allocates nothing (for callers that
+// cannot allocate: graph capture, tight loops): a fixed device array, one per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol); it takes each
+// device's address of it once, with hipGetSymbolAddress, and uses that.
+static __device__ __align__(256) uint8_t scratch[kEmbeddingStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t embedding_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dust

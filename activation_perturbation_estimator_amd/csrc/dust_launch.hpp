@@ -75,6 +75,10 @@ hipError_t launch_perturbed_linear(const void* X, const void* W, bool bf16, int6
 size_t embedding_workspace_bytes(int64_t T, int64_t N, int64_t vocab);
 hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, int64_t N,
                                  int64_t vocab, float* GE, void* workspace, hipStream_t s);
+// The library's own scratch for the variant that allocates nothing: the
+// current device's address of a fixed array of this many bytes.
+constexpr size_t kEmbeddingStaticScratchBytes = (size_t)16 << 20;
+hipError_t embedding_static_scratch(void** out);
 
 // Optimiser steps and the closed-form head gradient.
 hipError_t launch_sgd_momentum(float* W, const float* G, float* M, int64_t n, float lr, float mu,

@@ -19,7 +19,8 @@
  *   - Pointers named as device pointers are HIP device memory owned by the
  *     caller.  The library allocates nothing and keeps no state between calls,
  *     so calls on different streams may run concurrently (they must not share
- *     output or workspace buffers).
+ *     output or workspace buffers).  The one exception is
+ *     dust_embedding_grad_noalloc, whose scratch is a fixed array per GPU.
  *   - Calls enqueue kernels on the caller's stream `s` and return without
  *     waiting, except dust_check_targets, which waits for its own result.
  *     Outputs are overwritten, never accumulated.
@@ -233,6 +234,24 @@ dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t 
                                 int64_t vocab, float* G_E, void* workspace,
                                 size_t workspace_bytes, dust_stream_t s);
 size_t dust_embedding_workspace_size(int64_t T, int64_t N, int64_t vocab);
+
+/* dust_embedding_grad without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results (bitwise) as
+ * dust_embedding_grad; the scratch is the library's own fixed device array of
+ * DUST_EMBEDDING_NOALLOC_BYTES per GPU, held until the process ends, and the
+ * call allocates nothing.  Sizes whose scratch (dust_embedding_noalloc_bytes)
+ * exceeds it return DUST_ERR_UNSUPPORTED before any HIP call; the pages'
+ * embedding shape (16384 tokens, width 512, vocabulary 4096) needs about 2.7
+ * MiB.  Call with the stream's device current.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (different streams, or
+ * different host threads) race and give undefined results; calls ordered on
+ * one stream are safe, since each call writes every scratch byte it reads. */
+#define DUST_EMBEDDING_NOALLOC_BYTES ((size_t)16 << 20)
+dust_status dust_embedding_grad_noalloc(const int32_t* ids, const float* g_hat, int64_t T,
+                                        int64_t N, int64_t vocab, float* G_E, dust_stream_t s);
+/* Scratch bytes dust_embedding_grad_noalloc needs for a size (0 for invalid sizes). */
+size_t dust_embedding_noalloc_bytes(int64_t T, int64_t N, int64_t vocab);
 
 /* Optimiser steps on a weight gradient (linlog explainer, experiment setup:
  * SGD with momentum; paper digest, section 3.3: Adam).  All arrays device fp32

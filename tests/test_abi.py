@@ -168,3 +168,20 @@ def test_grid_and_overflow_limits():
     # outer product at widths whose tile grid alone exceeds 2^24 workgroups
     assert lib.dust_outer_sum(FAKE, FAKE, 1, 1024, 1 << 20, 1 << 20, FAKE, FAKE, 1 << 62,
                               None) == U
+
+
+def test_embedding_noalloc_rejections_and_size():
+    # host-side checks of the variant without a workspace: bad arguments, and
+    # sizes whose scratch exceeds the library's fixed array, before any HIP call
+    L, lib = _lib()
+    cap = 16 << 20
+    assert lib.dust_embedding_noalloc_bytes(16384, 512, 4096) < cap
+    assert (lib.dust_embedding_noalloc_bytes(16384, 512, 4096) + 256 ==
+            lib.dust_embedding_workspace_size(16384, 512, 4096))
+    assert lib.dust_embedding_noalloc_bytes(1 << 20, 1024, 64) > cap
+    assert lib.dust_embedding_noalloc_bytes(-1, 4, 4) == 0
+    f = lib.dust_embedding_grad_noalloc
+    assert f(FAKE, FAKE, 1 << 20, 1024, 64, FAKE, None) == L.DUST_ERR_UNSUPPORTED
+    assert f(None, FAKE, 8, 4, 4, FAKE, None) == L.DUST_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 8, 6, 4, FAKE, None) == L.DUST_ERR_INVALID_ARG  # N % 4
+    assert f(FAKE, FAKE, 8, 4, 0, FAKE, None) == L.DUST_ERR_INVALID_ARG
