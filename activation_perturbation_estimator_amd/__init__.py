@@ -167,10 +167,13 @@ def head_estimate(logits, targets, X, *, sigma: float, K: int, gamma: float = 0.
 
 
 def linear_estimate(X, c, *, N: int, sigma: float, gamma: float = 0.0, seed: int = 1,
-                    seq_len: Optional[int] = None, stream: int = 0,
-                    stage_events: Optional[Sequence] = None, workspace=None, out=None):
+                    seq_len: Optional[int] = None, stream: int = 0, draw0: int = 0,
+                    K_total: Optional[int] = None, stage_events: Optional[Sequence] = None,
+                    workspace=None, out=None):
     """Hidden linear layer: X [T,d_in] (f32/bf16), caller-centred loss decreases
-    c [K,T] f32 measured with dust noise (seed, stream, draws 0..K-1) of width N.
+    c [K,T] f32 measured with dust noise (seed, stream, draws draw0..draw0+K-1)
+    of width N, normalised by a population of K_total draws (default K), so
+    that calls over consecutive draw ranges add up.
     Returns (g_hat [T,N] f32, G_W [N,d_in] f32)."""
     T, d_in = X.shape
     K = c.shape[0]
@@ -184,7 +187,8 @@ def linear_estimate(X, c, *, N: int, sigma: float, gamma: float = 0.0, seed: int
     ws = _workspace(nbytes, dev, workspace)
     st = lib.dust_linear_estimate(
         _dev(X, "X"), _dtype_code(X), _dev(c, "c"), T, d_in, int(N), L, float(sigma), int(K),
-        float(gamma), int(seed), int(stream), _dev(g, "g_hat"), _dev(G, "G_W"), ws.data_ptr(),
+        float(gamma), int(seed), int(stream), int(draw0), int(K if K_total is None else K_total),
+        _dev(g, "g_hat"), _dev(G, "G_W"), ws.data_ptr(),
         ws.numel() * ws.element_size(), _stream(dev), _events(stage_events))
     _lib.check("dust_linear_estimate", st)
     return g, G
@@ -249,13 +253,17 @@ def reward_scan(c, *, seq_len: int, gamma: float, out=None):
     return r
 
 
-def error_estimate(r, *, N: int, sigma: float, seed: int = 1, stream: int = 0, out=None):
-    """g_hat[t,n] = -(1/(K sigma)) sum_i r[i,t] a^(i)_t[n] with regenerated noise."""
+def error_estimate(r, *, N: int, sigma: float, seed: int = 1, stream: int = 0, draw0: int = 0,
+                   K_total: Optional[int] = None, out=None):
+    """g_hat[t,n] = -(1/(K_total sigma)) sum_i r[i,t] a^(draw0+i)_t[n] with
+    regenerated noise (K_total defaults to K = r.shape[0])."""
     K, T = r.shape
     _expect(r, "r", dtypes=_f32())
     (g,) = _outputs(out, [(T, int(N))], r.device, ["out"])
     st = _lib.load().dust_error_estimate(_dev(r, "r"), K, T, int(N), float(sigma), int(seed),
-                                         int(stream), _dev(g, "g_hat"), _stream(r.device))
+                                         int(stream), int(draw0),
+                                         int(K if K_total is None else K_total), _dev(g, "g_hat"),
+                                         _stream(r.device))
     _lib.check("dust_error_estimate", st)
     return g
 

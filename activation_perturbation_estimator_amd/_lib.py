@@ -42,14 +42,15 @@ SIGNATURES = {
                                   _f32, _u64, _u32, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "dust_head_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _f32]),
     "dust_linear_estimate": (_int, [_vp, _int, _vp, _i64, _i64, _i64, _i64, _f32, _i64, _f32,
-                                    _u64, _u32, _vp, _vp, _vp, _sz, _vp, _vp]),
+                                    _u64, _u32, _i64, _i64, _vp, _vp, _vp, _sz, _vp, _vp]),
     "dust_linear_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _f32]),
     "dust_noise": (_int, [_u64, _u32, _i64, _i64, _i64, _i64, _vp, _vp]),
     "dust_philox4x32_10": (_int, [_u64, _vp, _vp, _i64, _vp]),
     "dust_head_losses": (_int, [_vp, _int, _vp, _i64, _i64, _f32, _i64, _u64, _u32, _vp, _vp]),
     "dust_centre": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "dust_reward_scan": (_int, [_vp, _i64, _i64, _i64, _f32, _vp, _vp]),
-    "dust_error_estimate": (_int, [_vp, _i64, _i64, _i64, _f32, _u64, _u32, _vp, _vp]),
+    "dust_error_estimate": (_int, [_vp, _i64, _i64, _i64, _f32, _u64, _u32, _i64, _i64, _vp,
+                                   _vp]),
     "dust_outer_sum": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "dust_outer_sum_workspace_size": (_sz, [_i64, _i64, _i64]),
     "dust_perturbed_linear": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _f32, _u64, _u32, _i64,

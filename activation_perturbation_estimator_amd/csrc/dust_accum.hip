@@ -20,8 +20,8 @@ namespace dust {
 template <int kNB, int kW>
 __global__ void __launch_bounds__(64 * kW)
 error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t N, float scale,
-                      uint32_t stream, uint32_t k0, uint32_t k1, float* __restrict__ g_hat,
-                      Gemm16Out op) {
+                      uint32_t stream, uint32_t draw0, uint32_t k0, uint32_t k1,
+                      float* __restrict__ g_hat, Gemm16Out op) {
   constexpr int kCols = 4 * kNB;
   __shared__ float red[3 * kW];
   const int lane = threadIdx.x & 63;
@@ -42,7 +42,7 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
     for (int b = 0; b < kNB; ++b) {
       const uint32_t j = (uint32_t)(b * 64 * kW + wave * 64 + lane);
       float a0, a1, a2, a3;
-      normal4_scaled<true>(j, (uint32_t)t, (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
+      normal4_scaled<true>(j, (uint32_t)t, draw0 + (uint32_t)i, stream, k0, k1, a0, a1, a2, a3);
       acc[4 * b] = fmaf(ri, a0, acc[4 * b]);
       acc[4 * b + 1] = fmaf(ri, a1, acc[4 * b + 1]);
       acc[4 * b + 2] = fmaf(ri, a2, acc[4 * b + 2]);
@@ -65,23 +65,24 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
 
 template <int kNB, int kW>
 static hipError_t launch_ee_t(const float* r, int64_t K, int64_t T, int64_t N, float scale,
-                              uint32_t stream, uint64_t seed, float* g_hat, const Gemm16Out& op,
-                              hipStream_t s) {
+                              uint32_t stream, uint64_t seed, uint32_t draw0, float* g_hat,
+                              const Gemm16Out& op, hipStream_t s) {
   hipLaunchKernelGGL((error_estimate_kernel<kNB, kW>), dim3((uint32_t)T), dim3(64 * kW), 0, s, r,
-                     K, T, N, scale, stream, (uint32_t)seed, (uint32_t)(seed >> 32), g_hat, op);
+                     K, T, N, scale, stream, draw0, (uint32_t)seed, (uint32_t)(seed >> 32), g_hat,
+                     op);
   return hipGetLastError();
 }
 
 hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
-                                 uint32_t stream, uint64_t seed, float* g_hat,
-                                 const Gemm16Out& op, hipStream_t s) {
+                                 uint32_t stream, uint64_t seed, uint32_t draw0, int64_t K_total,
+                                 float* g_hat, const Gemm16Out& op, hipStream_t s) {
   if (T == 0) return hipSuccess;
   // the noise comes divided by kBoxMullerScale (normal4_scaled)
-  const float scale = -kBoxMullerScale / ((float)K * sigma);
+  const float scale = -kBoxMullerScale / ((float)K_total * sigma);
   const HeadShape h = wide_shape(N);
 #define DUST_EE_CASE(NB, W) \
   if (h.nb == NB && h.w == W)                                                                  \
-    return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, g_hat, op, s);
+    return launch_ee_t<NB, W>(r, K, T, N, scale, stream, seed, draw0, g_hat, op, s);
   DUST_EE_CASE(1, 1)
   DUST_EE_CASE(2, 1)
   DUST_EE_CASE(4, 1)

@@ -38,6 +38,12 @@ constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 bool width_ok(int64_t N) { return N > 0 && N % 4 == 0 && N <= DUST_N_MAX; }
 
+// A range of draws draw0 .. draw0 + K - 1 of a population of K_total: the
+// draw is a 32-bit counter word of the noise.
+bool draws_ok(int64_t draw0, int64_t K, int64_t K_total) {
+  return draw0 >= 0 && K_total >= 1 && K_total <= kMaxK && draw0 <= ((int64_t)1 << 32) - K;
+}
+
 // a * b <= lim for a, b >= 0, without forming a product that could overflow.
 bool prod_le(int64_t a, int64_t b, int64_t lim) { return b == 0 || a <= lim / b; }
 
@@ -164,7 +170,7 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
         (e = dust::launch_reward_scan(delta, K, T, seq_len, gamma, delta, s)) != hipSuccess)
       return DUST_ERR_HIP;
     if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
-    e = dust::launch_error_estimate(delta, K, T, V, sigma, stream, seed, g_hat, op, s);
+    e = dust::launch_error_estimate(delta, K, T, V, sigma, stream, seed, 0, K, g_hat, op, s);
     if (e != hipSuccess) return DUST_ERR_HIP;
     if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
   }
@@ -175,10 +181,12 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt, const i
 
 dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c, int64_t T,
                                  int64_t d_in, int64_t N, int64_t seq_len, float sigma, int64_t K,
-                                 float gamma, uint64_t seed, uint32_t stream, float* g_hat,
-                                 float* G_W, void* workspace, size_t workspace_bytes,
-                                 dust_stream_t s_, const dust_event_t* stage_events) {
+                                 float gamma, uint64_t seed, uint32_t stream, int64_t draw0,
+                                 int64_t K_total, float* g_hat, float* G_W, void* workspace,
+                                 size_t workspace_bytes, dust_stream_t s_,
+                                 const dust_event_t* stage_events) {
   if (!X || !c || !g_hat || !G_W || !dtype_ok(x_dt)) return DUST_ERR_INVALID_ARG;
+  if (!draws_ok(draw0, K, K_total)) return DUST_ERR_INVALID_ARG;
   if (T <= 0 || !width_ok(N) || d_in <= 0 || K <= 0 || K > kMaxK) return DUST_ERR_INVALID_ARG;
   if (T > kMaxT || d_in > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (seq_len <= 0 || T % seq_len != 0) return DUST_ERR_INVALID_ARG;
@@ -204,8 +212,8 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
   }
   if ((e = record(stage_events, 1, s)) != hipSuccess) return DUST_ERR_HIP;
   const dust::Gemm16Out op = dust::outer_sum_operands(gemm_ws, T, N, d_in, X, x_dt == DUST_BF16);
-  if ((e = dust::launch_error_estimate(rr, K, T, N, sigma, stream, seed, g_hat, op, s)) !=
-      hipSuccess)
+  if ((e = dust::launch_error_estimate(rr, K, T, N, sigma, stream, seed, (uint32_t)draw0,
+                                      K_total, g_hat, op, s)) != hipSuccess)
     return DUST_ERR_HIP;
   if ((e = record(stage_events, 2, s)) != hipSuccess) return DUST_ERR_HIP;
   if ((e = dust::launch_outer_sum16(op, g_hat, N, G_W, gemm_ws, s)) != hipSuccess)
@@ -255,13 +263,16 @@ dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_l
 }
 
 dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
-                                uint64_t seed, uint32_t stream, float* g_hat, dust_stream_t s) {
+                                uint64_t seed, uint32_t stream, int64_t draw0, int64_t K_total,
+                                float* g_hat, dust_stream_t s) {
   if (!r || !g_hat || K <= 0 || K > kMaxK || T <= 0 || !width_ok(N) || !sigma_ok(sigma))
     return DUST_ERR_INVALID_ARG;
+  if (!draws_ok(draw0, K, K_total)) return DUST_ERR_INVALID_ARG;
   if (T > kMaxTokens || T * N > kMaxElems || K * T > kMaxElems) return DUST_ERR_UNSUPPORTED;
   const dust::Gemm16Out none{};  // no G_W operands wanted
   return hip_status(
-      dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, g_hat, none, as_stream(s)));
+      dust::launch_error_estimate(r, K, T, N, sigma, stream, seed, (uint32_t)draw0, K_total,
+                                  g_hat, none, as_stream(s)));
 }
 
 dust_status dust_outer_sum(const float* g_hat, const void* X, dust_dtype x_dt, int64_t T,

@@ -49,9 +49,10 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
                               float* r, hipStream_t s);
 
 // Error estimate from rewards with regenerated noise.
+// Draws draw0 .. draw0 + K - 1 of a population of K_total (the 1/(K_total sigma)).
 hipError_t launch_error_estimate(const float* r, int64_t K, int64_t T, int64_t N, float sigma,
-                                 uint32_t stream, uint64_t seed, float* g_hat,
-                                 const Gemm16Out& op, hipStream_t s);
+                                 uint32_t stream, uint64_t seed, uint32_t draw0, int64_t K_total,
+                                 float* g_hat, const Gemm16Out& op, hipStream_t s);
 
 // Outer-product sum G = g^T X on the matrix cores.  The workspace starts with
 // the fp16 operands (outer_sum_operands), written either by the kernel that

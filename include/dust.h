@@ -133,18 +133,25 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt,
 size_t dust_head_workspace_size(int64_t T, int64_t V, int64_t d, int64_t K, float gamma);
 
 /* Hidden linear layer y = W x (paper digest, section 2.2): the caller ran its
- * K perturbed forwards with noise from dust_noise(seed, stream, 0, K, T, N)
- * and measured c[i,t], the centred loss decrease of token t under draw i.  c
- * is used as given (the library does not centre it).
+ * perturbed forwards with noise from dust_noise(seed, stream, draw0, K, T, N)
+ * and measured c[i,t], the centred loss decrease of token t under draw
+ * draw0 + i.  c is used as given (the library does not centre it).
  *   X      device [T,d_in], dtype x_dt
- *   c      device [K,T] fp32
+ *   c      device [K,T] fp32: draws draw0 .. draw0 + K - 1
+ *   draw0, K_total  this call's draws are draw0 .. draw0 + K - 1 of a
+ *          population of K_total draws, the K of the estimate's 1/(K sigma):
+ *          g_t = -(1/(K_total sigma)) sum_{i<K} r^(i)_t a^(draw0+i)_t.  The
+ *          estimate of a population therefore splits into draw ranges whose
+ *          results add up (restart, or several calls over one population);
+ *          draw0 = 0, K_total = K is the whole estimate.  Requires draw0 >= 0,
+ *          K_total >= 1, draw0 + K <= 2^32 (the draw is a 32-bit counter word).
  *   g_hat  device [T,N] fp32 out;  G_W device [N,d_in] fp32 out
  * Same rules as above for sigma, K, gamma, seq_len, N % 4, workspace and
  * stage_events ([1] after the gamma scan). */
 dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
                                  int64_t T, int64_t d_in, int64_t N, int64_t seq_len,
                                  float sigma, int64_t K, float gamma,
-                                 uint64_t seed, uint32_t stream,
+                                 uint64_t seed, uint32_t stream, int64_t draw0, int64_t K_total,
                                  float* g_hat, float* G_W,
                                  void* workspace, size_t workspace_bytes,
                                  dust_stream_t s, const dust_event_t* stage_events);
@@ -187,10 +194,13 @@ dust_status dust_reward_scan(const float* c, int64_t K, int64_t T, int64_t seq_l
                              float gamma, float* r, dust_stream_t s);
 
 /* Error estimate (paper digest, section 2.2):
- * g_hat[t,n] = -(1/(K sigma)) sum_i r[i,t] a^(i)_t[n], the noise regenerated
- * from (seed, stream).  r device [K,T] fp32; g_hat device [T,N] fp32 out. */
+ * g_hat[t,n] = -(1/(K_total sigma)) sum_{i<K} r[i,t] a^(draw0+i)_t[n], the
+ * noise regenerated from (seed, stream); draw0 and K_total as for
+ * dust_linear_estimate (draw0 = 0, K_total = K: the whole estimate).
+ *   r device [K,T] fp32; g_hat device [T,N] fp32 out. */
 dust_status dust_error_estimate(const float* r, int64_t K, int64_t T, int64_t N,
                                 float sigma, uint64_t seed, uint32_t stream,
+                                int64_t draw0, int64_t K_total,
                                 float* g_hat, dust_stream_t s);
 
 /* Weight gradient (paper digest, section 2.2): G_W[n,k] = sum_t g_hat[t,n] X[t,k].

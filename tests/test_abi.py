@@ -89,14 +89,16 @@ def test_linear_estimate_rejects():
     L, lib = _lib()
     def call(**kw):
         a = dict(X=FAKE, xdt=1, c=FAKE, T=4096, d_in=512, N=2048, L=2048, sigma=0.01, K=8,
-                 gamma=0.9, seed=1, stream=0, g=FAKE, G=FAKE, ws=FAKE, wsb=1 << 40)
+                 gamma=0.9, seed=1, stream=0, draw0=0, K_total=8, g=FAKE, G=FAKE, ws=FAKE,
+                 wsb=1 << 40)
         a.update(kw)
         return lib.dust_linear_estimate(a["X"], a["xdt"], a["c"], a["T"], a["d_in"], a["N"],
                                         a["L"], a["sigma"], a["K"], a["gamma"], a["seed"],
-                                        a["stream"], a["g"], a["G"], a["ws"], a["wsb"], None,
-                                        None)
+                                        a["stream"], a["draw0"], a["K_total"], a["g"], a["G"],
+                                        a["ws"], a["wsb"], None, None)
     for bad in (dict(X=None), dict(c=None), dict(N=2046), dict(L=1000), dict(K=0),
-                dict(gamma=2.0), dict(sigma=0.0), dict(d_in=0)):
+                dict(gamma=2.0), dict(sigma=0.0), dict(d_in=0), dict(draw0=-1),
+                dict(K_total=0), dict(draw0=(1 << 32) - 7)):
         assert call(**bad) == L.DUST_ERR_INVALID_ARG, bad
     assert call(wsb=16) == L.DUST_ERR_WORKSPACE
 
@@ -115,7 +117,10 @@ def test_stage_calls_reject():
     assert lib.dust_centre(FAKE, 0, 8, FAKE, None) == E
     assert lib.dust_reward_scan(FAKE, 4, 10, 3, 0.5, FAKE, None) == E  # T % L
     assert lib.dust_reward_scan(FAKE, 4, 12, 3, 1.5, FAKE, None) == E
-    assert lib.dust_error_estimate(FAKE, 4, 8, 10, 0.1, 1, 0, FAKE, None) == E
+    assert lib.dust_error_estimate(FAKE, 4, 8, 10, 0.1, 1, 0, 0, 4, FAKE, None) == E
+    assert lib.dust_error_estimate(FAKE, 4, 8, 8, 0.1, 1, 0, -1, 4, FAKE, None) == E
+    assert lib.dust_error_estimate(FAKE, 4, 8, 8, 0.1, 1, 0, 0, 0, FAKE, None) == E
+    assert lib.dust_error_estimate(FAKE, 4, 8, 8, 0.1, 1, 0, (1 << 32) - 3, 4, FAKE, None) == E
     assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, 0, 4, FAKE, FAKE, 1 << 30, None) == E
     assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, 4, 4, FAKE, None, 0, None) == L.DUST_ERR_WORKSPACE
     assert lib.dust_check_targets(None, 8, 4, FAKE, None) == E
@@ -141,7 +146,7 @@ def test_size_limits_are_unsupported_not_invalid():
     assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, (1 << 20) + 4, 4, FAKE, FAKE, 1 << 40, None) == U
     assert lib.dust_outer_sum(FAKE, FAKE, 0, 8, 4, (1 << 20) + 8, FAKE, FAKE, 1 << 40, None) == U
     assert lib.dust_linear_estimate(FAKE, 1, FAKE, 4096, (1 << 20) + 8, 2048, 2048, 0.01, 8,
-                                    0.9, 1, 0, FAKE, FAKE, FAKE, 1 << 40, None, None) == U
+                                    0.9, 1, 0, 0, 8, FAKE, FAKE, FAKE, 1 << 40, None, None) == U
 
 
 def test_grid_and_overflow_limits():
@@ -151,7 +156,7 @@ def test_grid_and_overflow_limits():
     L, lib = _lib()
     U = L.DUST_ERR_UNSUPPORTED
     big = 1 << 24                                      # one workgroup per token: T < 2^24
-    assert lib.dust_error_estimate(FAKE, 2, big, 4, 0.1, 1, 0, FAKE, None) == U
+    assert lib.dust_error_estimate(FAKE, 2, big, 4, 0.1, 1, 0, 0, 2, FAKE, None) == U
     assert lib.dust_head_losses(FAKE, 0, FAKE, big, 4, 0.1, 2, 1, 0, FAKE, None) == U
     assert lib.dust_centre(FAKE, 1, big, FAKE, None) == U
     assert lib.dust_ce_grad(FAKE, 0, FAKE, big, 4, FAKE, None) == U

@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 from activation_perturbation_estimator_amd import synth
-from util import (G_HAT_TERM_TOL, assert_elementwise, assert_gw, assert_parity, assert_rows,
-                  need_gpu)
+from util import (G_HAT_TERM_TOL, G_W_RSS_TOL, assert_elementwise, assert_gw, assert_parity,
+                  assert_rows, gw_rss_scale, need_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,3 +61,49 @@ def test_one_hot_closed_form():
         outside = np.ones(T, bool)
         outside[(s_s // L) * L:s_s + 1] = False
         assert np.all(g[outside] == 0)
+
+
+@pytest.mark.parametrize("gamma,bf16", [(0.0, True), (0.9, False)])
+def test_draw_ranges_add_up(gamma, bf16):
+    """The population [0, K) split at k: calls over draws [0, k) and [k, K),
+    each normalised by the whole population (K_total = K), add up to the whole
+    estimate, which the oracle computes in one piece."""
+    dust = need_gpu()
+    T, L, d, N, K, k = 256, 64, 40, 300, 40, 17
+    X, c = synth.linear_inputs(T, d, K, seed=31, c_seed=5, bf16=bf16)
+    kw = dict(N=N, sigma=0.02, gamma=gamma, seed=7, seq_len=L, stream=2)
+    g1, G1 = _run(dust, X, c[:k].contiguous(), draw0=0, K_total=K, **kw)
+    g2, G2 = _run(dust, X, c[k:].contiguous(), draw0=k, K_total=K, **kw)
+    rg, rG, sc = oracle.linear_estimate(synth.to_f64(X), c.double().numpy(), L, N, 0.02, gamma, 7,
+                                        2, with_scale=True)
+    g = g1.astype(np.float64) + g2
+    assert_parity(g, rg, "g_hat from two draw ranges")
+    assert_rows(g, rg, "g_hat rows from two draw ranges")
+    assert_elementwise(g, rg, sc, "g_hat elements from two draw ranges", G_HAT_TERM_TOL)
+    G = G1.astype(np.float64) + G2
+    assert_parity(G, rG, "G_W from two draw ranges")
+    X64 = synth.to_f64(X)
+    scale = np.sqrt(gw_rss_scale(g1, X64) ** 2 + gw_rss_scale(g2, X64) ** 2)
+    assert_elementwise(G, rG, scale, "G_W elements from two draw ranges", G_W_RSS_TOL,
+                       atol=1e-6 * float(np.abs(rG).max()))
+
+
+def test_one_hot_closed_form_at_a_draw_offset():
+    """c one-hot at draw i* of a call whose draws start at draw0 = 5 in a
+    population of 12: g_t = -(1/(12 sigma)) gamma^(s*-t) a^(5+i*)_t."""
+    dust = need_gpu()
+    import torch
+    T, L, N, K, d, sigma, gamma, seed, draw0, K_total = 48, 16, 24, 4, 8, 0.05, 0.7, 9, 5, 12
+    a = oracle.noise(seed, 0, draw0, K, T, N)
+    X = torch.ones((T, d), dtype=torch.float32)
+    c = torch.zeros((K, T), dtype=torch.float32)
+    i_s, s_s = 2, 29
+    c[i_s, s_s] = 1.0
+    g, _ = _run(dust, X, c, N=N, sigma=sigma, gamma=gamma, seed=seed, seq_len=L, draw0=draw0,
+                K_total=K_total)
+    ref = np.zeros((T, N))
+    for t in range((s_s // L) * L, s_s + 1):
+        ref[t] = -(gamma ** (s_s - t)) * a[i_s, t] / (K_total * sigma)
+    assert_parity(g, ref, "g_hat one-hot at a draw offset")
+    assert_elementwise(g, ref, np.abs(ref), "g_hat one-hot at a draw offset", 1e-5,
+                       atol=1e-5 / (K_total * sigma))

@@ -121,6 +121,25 @@ def _check_outer(G, ref, g, X64):
                        atol=1e-6 * float(np.abs(ref).max()))
 
 
+def test_error_estimate_draw_ranges():
+    """dust_error_estimate over draws [0, k) and [k, K) of a population of K
+    adds up to the call over [0, K)."""
+    dust = need_gpu()
+    import torch
+    K, T, N, k = 30, 40, 520, 11
+    r = torch.from_numpy(np.random.default_rng(3).standard_normal((K, T)).astype(np.float32) * 0.03)
+    full = dust.error_estimate(_cuda(r), N=N, sigma=0.02, seed=4, stream=1)
+    a = dust.error_estimate(_cuda(r[:k]), N=N, sigma=0.02, seed=4, stream=1, K_total=K)
+    b = dust.error_estimate(_cuda(r[k:]), N=N, sigma=0.02, seed=4, stream=1, draw0=k, K_total=K)
+    torch.cuda.synchronize()
+    ref, sc = oracle.linear_rows(r.double().numpy(), T, N, 0.02, 0.0, 4, list(range(T)), 1,
+                                 with_scale=True)
+    for got, what in ((full.cpu().numpy(), "whole"),
+                      (a.cpu().double().numpy() + b.cpu().double().numpy(), "two ranges")):
+        assert_parity(got, ref, what)
+        assert_elementwise(got, ref, sc, what, G_HAT_TERM_TOL)
+
+
 @pytest.mark.parametrize("T,N,d,bf16", [(600, 1000, 72, True), (600, 1000, 72, False),
                                          (1, 5, 3, False), (4097, 300, 129, True),
                                          (2048, 512, 512, True), (31, 64, 64, False),
