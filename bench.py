@@ -12,8 +12,11 @@ bounded sample of the same workload.
   python bench.py [--steps 10] [--warmup 2] [--workload paper] [--no-cpu-baseline]
                   [--copy-probe-mib 256]
 
-Other workloads print their own line: linear (the hidden-layer estimator),
-forward (perturbed forward), embedding, optim (SGD/Adam steps), cosine (the
+The default line also carries sub-records ("workloads") for the K = 16384 LM
+head (the public code's default population) and the hidden-layer estimator,
+each with its own roofline and oracle baseline.  Other workloads print their
+own line: linear (the hidden-layer estimator), k1024, k16384, forward
+(perturbed forward), embedding, optim (SGD/Adam steps), cosine (the
 cosine-versus-population sweep and its fitted law).
 """
 from __future__ import annotations
@@ -36,21 +39,33 @@ VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
 FP16_MFMA_FLOPS = 2.5e15  # dense fp16 (and bf16) matrix cores
 HBM_BYTES_PER_S = 8.0e12
 
-# Algorithmic VALU issue slots per normal (one column of one token-draw) of
-# the fused gamma = 0 head kernel.  Issue cost on gfx950, measured with a
-# dependent-chain probe: 1 slot for fp32 add/mul/fma and 32-bit logic
-# (including v_bitop3), 2 for v_mad_u64_u32 and v_alignbit, 4 for the
-# transcendentals (v_exp, v_log, v_sqrt, v_sin, v_cos).
-#   Philox4x32-10 per block of 4 normals, counter (token, column/4, draw,
-#     stream): 16 lane-varying 32x32->64 products (2) + 18 xors (1) = 50 -> 12.5
+# VALU issue slots per normal (one column of one token-draw), charged at the
+# issue costs measured on gfx950 with a dependent-chain probe: 1 slot for fp32
+# add/mul/fma and 32-bit logic (including v_bitop3), 2 for v_mad_u64_u32 and
+# v_alignbit, 4 for the transcendentals (v_exp, v_log, v_sqrt, v_sin, v_cos).
+#
+# Algorithmic count, the work the method itself asks per normal (what the
+# roofline divides by):
+#   Philox4x32-10, a quarter block: 5 32x32->64 products (2) + 5 three-input
+#     xors (1) = 15
 #   uniform map: alignbit + subtract = 3
-#   Box-Muller per pair: log, sqrt, cos, sin (4 each) + 2 multiplies (radius times
-#     cosine and sine; the constant sqrt(2 ln 2) of the radius rides on sigma) = 18 -> 9
+#   Box-Muller, half a pair: half of log, sqrt, sin, cos (8) + the radius
+#     multiply (1) = 9
 #   perturbed cross-entropy: FMA + exp2 + add = 6
 #   accumulation of sum a and sum delta a: 2
-SLOTS = {"philox": (16 * 2 + 18) / 4, "uniform": 3, "box_muller": (4 * 4 + 2) / 2,
-         "cross_entropy": 6, "accumulate": 2}
+# total 35.  The error estimate of the linear layer: the same noise (27) and
+# one FMA, 28.
+SLOTS = {"philox": 15.0, "uniform": 3.0, "box_muller": 9.0, "cross_entropy": 6.0,
+         "accumulate": 2.0}
 SLOTS_PER_NORMAL = sum(SLOTS.values())
+SLOTS_PER_NORMAL_ERROR_ESTIMATE = SLOTS["philox"] + SLOTS["uniform"] + SLOTS["box_muller"] + 1
+# The fused head kernel's own count is lower: with the column's Philox word in
+# a xor, the first rounds are the same for all lanes of a wave and 4 of the 20
+# products per block run on the scalar unit (16 x 2 + 18 xors = 12.5 per
+# normal), and the normals come scaled by 1/sqrt(2 ln 2), one multiply fewer
+# per pair (Box-Muller 9): 32.5 slots issued per normal by design.
+IMPL_SLOTS_PER_NORMAL = 32.5
+IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE = 25.5
 
 # Hardware byte counts of the head kernel (FETCH_SIZE and WRITE_SIZE from two
 # rocprofv3 --pmc runs, scaled by the same counters read on a plain copy of
@@ -97,6 +112,8 @@ def parse():
                          "linear (hidden layer 512->2048, K=256, gamma=0.9); the other rows: "
                          "forward, embedding, optim, cosine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-workloads", action="store_true",
+                    help="paper workload only: skip the K=16384 and linear sub-records")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -105,30 +122,64 @@ def parse():
     return ap.parse_args()
 
 
+def host_cores() -> int:
+    """The cores this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def oracle_rate(run_sample, T: int, K: int, target_s: float, threads: int, n0: int):
+    """Time the oracle (as it stands) on growing random token samples of the
+    workload (all K draws each, seed 1) until one takes about target_s seconds
+    on `threads` OpenMP threads; returns (token-draws/s, tokens, seconds)."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    oracle.set_num_threads(threads)
+    rng = np.random.default_rng(1)
+    n = max(1, min(n0, T))
+    while True:
+        tok = np.sort(rng.choice(T, size=n, replace=False))
+        t0 = time.perf_counter()
+        run_sample(tok)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= T:
+            break
+        n = min(T, max(n + 1, int(n * min(8.0, 0.75 * target_s / max(dt, 1e-3)))))
+    return len(tok) * K / dt, len(tok), dt
+
+
+def cpu_baseline_record(run_sample, w, target_s: float, what: str):
+    """The oracle on all host cores and on one thread, on bounded samples of the
+    same workload; the rate is per token-draw, uniform over tokens, so the full
+    workload's time is the sample's scaled by T / tokens ("extrapolated")."""
+    cores = host_cores()
+    rate, ntok, dt = oracle_rate(run_sample, w.T, w.K, target_s, cores, 2 * cores)
+    rate1, ntok1, dt1 = oracle_rate(run_sample, w.T, w.K, target_s / 2, 1, 1)
+    return {"value": rate, "unit": "token-draws/s", "cores": cores, "kind": "oracle",
+            "sample": f"{ntok} of {w.T} tokens x all {w.K} draws of the same workload ({what}, "
+                      f"fp64, OpenMP over tokens on {cores} threads), {dt:.2f} s; full workload "
+                      f"extrapolated: {w.T * w.K / rate:.1f} s",
+            "single_thread": {"value": rate1, "cores": 1,
+                              "sample": f"{ntok1} tokens x {w.K} draws, {dt1:.2f} s"}}
+
+
 def cpu_baseline(w, z, y, target_s: float):
-    """The fp64 oracle, as it stands, on a bounded sample of tokens of the same
-    workload (all K draws per token, every host core)."""
+    """The fp64 oracle, as it stands, on bounded samples of tokens of the same
+    LM-head workload."""
     import numpy as np
     import oracle
     from activation_perturbation_estimator_amd import synth
-    oracle.build(force=False)
-    cores = oracle.num_threads()
-    rng = np.random.default_rng(1)
-    n = max(cores, 8)
-    while True:
-        tok = np.sort(rng.choice(w.T, size=min(n, w.T), replace=False))
+    yn = y.numpy()
+
+    def run(tok):
         zfull = np.zeros((w.T, w.V))
         zfull[tok] = synth.to_f64(z[tok])
-        t0 = time.perf_counter()
-        oracle.head_rows(zfull, y.numpy(), w.seq_len, w.sigma, w.K, w.gamma, w.philox_seed, tok)
-        dt = time.perf_counter() - t0
-        if dt >= target_s or n >= w.T or dt * 2 * (target_s / max(dt, 1e-3)) > 6 * target_s:
-            break
-        n = min(w.T, int(n * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
-    td = len(tok) * w.K
-    return {"value": td / dt, "unit": "token-draws/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(tok)} of {w.T} tokens x all {w.K} draws of the same workload "
-                      f"(g_hat rows, fp64, OpenMP over tokens), {dt:.2f} s"}
+        oracle.head_rows(zfull, yn, w.seq_len, w.sigma, w.K, w.gamma, w.philox_seed, tok)
+
+    return cpu_baseline_record(run, w, target_s, "g_hat rows")
 
 
 def time_steps(torch, step, steps: int, warmup: int, nev: int, copy_probe_mib: int = 0):
@@ -210,7 +261,10 @@ def run_head(args, torch, dust, synth, w):
                        if fused else "head_kernel (per-draw losses)",
                        "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
                        "frac": achieved / peak, "traffic": measured_traffic(w.name),
-                       "slots_per_normal": SLOTS_PER_NORMAL, "launch_ms": head_ms}
+                       "slots_per_normal": SLOTS_PER_NORMAL,
+                       "impl_slots_per_normal": IMPL_SLOTS_PER_NORMAL,
+                       "impl_frac": achieved / peak * IMPL_SLOTS_PER_NORMAL / SLOTS_PER_NORMAL,
+                       "launch_ms": head_ms}
     # the same kernel in HBM terms (algorithmic bytes: logits read once, g_hat written once)
     head_bytes = w.T * w.V * (2.0 if w.bf16 else 4.0) + 4.0 * w.T + 4.0 * w.T * w.V
     out["roofline"]["hbm_gbs"] = head_bytes / (head_ms / 1e3) / 1e9
@@ -222,31 +276,14 @@ def run_head(args, torch, dust, synth, w):
     return out
 
 
-# Error-estimate kernel, per normal: the noise (Philox 12.5 + uniform map 3 +
-# Box-Muller 9.5 slots) and one FMA.
-SLOTS_PER_NORMAL_ERROR_ESTIMATE = SLOTS["philox"] + SLOTS["uniform"] + SLOTS["box_muller"] + 1
-
-
 def cpu_baseline_linear(w, c, target_s: float):
-    import numpy as np
     import oracle
-    oracle.build(force=False)
-    cores = oracle.num_threads()
     cd = c.double().numpy()
-    rng = np.random.default_rng(1)
-    n = max(cores, 8)
-    while True:
-        tok = np.sort(rng.choice(w.T, size=min(n, w.T), replace=False))
-        t0 = time.perf_counter()
+
+    def run(tok):
         oracle.linear_rows(cd, w.seq_len, w.V, w.sigma, w.gamma, w.philox_seed, tok)
-        dt = time.perf_counter() - t0
-        if dt >= target_s or n >= w.T or dt * 2 * (target_s / max(dt, 1e-3)) > 6 * target_s:
-            break
-        n = min(w.T, int(n * max(2.0, min(8.0, target_s / max(dt, 1e-3)))))
-    return {"value": len(tok) * w.K / dt, "unit": "token-draws/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{len(tok)} of {w.T} tokens x all {w.K} draws of the same workload "
-                      f"(reward scan over all tokens, g_hat rows, fp64), {dt:.2f} s"}
+
+    return cpu_baseline_record(run, w, target_s, "reward scan over all tokens, g_hat rows")
 
 
 def run_linear(args, torch, dust, synth, w):
@@ -278,7 +315,10 @@ def run_linear(args, torch, dust, synth, w):
     out["roofline"] = {"bound": "alu", "kernel": "error_estimate_kernel (noise + r a accumulate)",
                        "achieved": achieved, "peak": peak, "unit": "T VALU slots/s",
                        "frac": achieved / peak, "traffic": None,
-                       "slots_per_normal": SLOTS_PER_NORMAL_ERROR_ESTIMATE, "launch_ms": ee_ms}
+                       "slots_per_normal": SLOTS_PER_NORMAL_ERROR_ESTIMATE,
+                       "impl_slots_per_normal": IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE,
+                       "impl_frac": achieved / peak * IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE /
+                       SLOTS_PER_NORMAL_ERROR_ESTIMATE, "launch_ms": ee_ms}
     # the accumulate pass in HBM terms too: it reads r [K,T] and writes g_hat [T,N]
     acc_bytes = 4.0 * w.K * w.T + 4.0 * w.T * w.V
     out["roofline"]["hbm_gbs"] = acc_bytes / (ee_ms / 1e3) / 1e9
@@ -422,6 +462,28 @@ ROWS = {"forward": run_forward, "embedding": run_embedding, "optim": run_optim,
         "cosine": run_cosine}
 
 
+# The default line's sub-records: the public code's default population (the
+# largest single-GPU head workload) and the hidden-layer estimator, each with
+# its own roofline and oracle baseline (steps, oracle seconds).
+SUB_WORKLOADS = (("k16384", 3, 4.0), ("linear", 10, 4.0))
+SUB_KEEP = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "config", "roofline",
+            "stages_ms", "outer_sum", "reward_scan", "cpu_baseline")
+
+
+def run_sub_workloads(args, torch, dust, synth):
+    import copy
+    subs = {}
+    for name, steps, cpu_s in SUB_WORKLOADS:
+        a = copy.copy(args)
+        a.steps, a.warmup, a.cpu_seconds, a.copy_probe_mib = steps, 1, cpu_s, 0
+        w = synth.WORKLOADS[name]
+        run = run_linear if w.kind == "linear" else run_head
+        print(f"[bench] {name}: {steps} steps", file=sys.stderr, flush=True)
+        rec = run(a, torch, dust, synth, w)
+        subs[name] = {k: v for k, v in rec.items() if k in SUB_KEEP}
+    return subs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -438,7 +500,10 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     run = run_linear if w.kind == "linear" else run_head
-    print(json.dumps(run(args, torch, dust, synth, w)), flush=True)
+    rec = run(args, torch, dust, synth, w)
+    if args.workload == "paper" and not args.no_sub_workloads:
+        rec["workloads"] = run_sub_workloads(args, torch, dust, synth)
+    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":
