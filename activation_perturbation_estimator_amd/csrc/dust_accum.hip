@@ -26,7 +26,7 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
   __shared__ float red[3 * kW];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t = blockIdx.x;
+  const int64_t t = producer_token(blockIdx.x, T);
   const int64_t nblk = N >> 2;
 
   float acc[kCols];

@@ -86,6 +86,18 @@ __device__ __forceinline__ void group_max3(float& a, float& b, float& c, float* 
   }
 }
 
+// Token of workgroup b in a grid of T workgroups that produce one token each.
+// Workgroups are dealt to the 8 XCDs in turn (XCD b % 8), and the 8 tokens of
+// one x16 group write interleaved 2-byte slots of the same lines, so within
+// each full block of 64 tokens the (turn, XCD) grid is transposed: XCD x then
+// produces tokens 8x .. 8x+7 of the block, and its L2 merges their writes into
+// whole lines instead of 8 XCDs each writing the lines back partially. Tokens
+// past the last full block keep b.
+__device__ __forceinline__ int64_t producer_token(uint32_t b, int64_t T) {
+  if ((int64_t)b >= (T & ~(int64_t)63)) return (int64_t)b;
+  return (int64_t)(b & ~63u) + 8 * (int64_t)(b & 7u) + (int64_t)((b >> 3) & 7u);
+}
+
 // Scaled copy of x_t into its column slots of x16 (every thread of the
 // token's workgroup, threads striding over the columns), and the zero
 // padding of the last token group when t is the last token.

@@ -132,7 +132,7 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t = blockIdx.x;
+  const int64_t t = producer_token(blockIdx.x, T);
   const int64_t nblk = V >> 2;
   const ZT* zrow = logits + t * V;
 

@@ -3,7 +3,8 @@
   python -m activation_perturbation_estimator_amd.probes [valu|gemm] [--build-only]
 
 valu: issue rates of the VALU instructions the estimator kernels use.
-gemm: bf16 MFMA rate, LDS read and LDS-load rates, and the G_W inner loop.
+gemm: bf16 and fp16 MFMA rates, LDS read and LDS-load rates, and the fp16 G_W
+inner loop.
 """
 import os
 import subprocess

@@ -1,8 +1,7 @@
 // gemm_rates.hip -- throughput probes behind the design of the G_W kernel on
-// gfx950: the bf16 matrix-core rate, the LDS read rates of the instruction
-// forms the kernel can use, the rate of buffer loads that write LDS directly,
-// and the G_W inner loop in isolation (LDS operands, MFMA), with the fp32 ->
-// bf16 hi/lo split done in the loop or not.  Build and run:
+// gfx950: the bf16 and fp16 matrix-core rates, the LDS read rates of the
+// instruction forms the kernel can use, the rate of buffer loads that write
+// LDS directly, and the fp16 G_W inner loop in isolation (LDS operands, MFMA).  Build and run:
 //   python -m activation_perturbation_estimator_amd.probes gemm
 // Every LDS address stays inside the kernel's own shared array; the loaded
 // buffer is 1 MiB and every load offset stays below 8 KiB.
@@ -13,7 +12,6 @@
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
@@ -21,13 +19,6 @@ typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x2_t lds_f32x2;
 typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const f32x2_t v = {a, b};
-  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-  const f32x2_t r = {a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u)};
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-}
 
 // 1. Matrix cores alone: 16 independent v_mfma_f32_32x32x16_bf16 per iteration.
 __global__ void __launch_bounds__(256) mfma_only(float* out, int iters) {
@@ -149,12 +140,16 @@ __global__ void __launch_bounds__(256) lds_dma(const float* src, float* out, int
   out[blockIdx.x * 256 + threadIdx.x] = reinterpret_cast<float*>(lds)[threadIdx.x];
 }
 
-// 4. The G_W inner loop in isolation, per 16 tokens and wave: A = 2 blocks of
-// 32 rows (fp32, eight b32 reads each, split into hi/lo in the loop) or, with
-// kPlanes, the same blocks as pre-split bf16 planes (transposed reads, no
-// VALU); B = 4 blocks by transposed reads; 16 MFMAs.
-template <bool kPlanes>
-__global__ void __launch_bounds__(256, 1) gw_loop(float* out, int iters) {
+// 4. The G_W inner loop in isolation, per 16 tokens and wave (a 64 x 128 wave
+// tile): A = 2 blocks of 32 rows of the token-major fp16 g operand, each by
+// two transposed reads (ds_read_b64_tr_b16); B = 4 blocks of 32 columns of the
+// 8-token-blocked fp16 x operand, one ds_read_b128 each; 8 MFMAs.  Two such
+// steps per iteration (32 tokens, as one LDS stage of the kernel).  With
+// kReads false the operands are read once before the loop, which leaves the
+// matrix instructions and the loop's own overhead.
+typedef __attribute__((address_space(3))) f16x8_t lds_f16x8;
+template <bool kReads>
+__global__ void __launch_bounds__(256) gw16_loop(float* out, int iters) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
   for (int i = threadIdx.x; i < 16384; i += 256) reinterpret_cast<float*>(lds)[i] = 0.001f * (i & 7);
   __syncthreads();
@@ -163,53 +158,29 @@ __global__ void __launch_bounds__(256, 1) gw_loop(float* out, int iters) {
   for (int x = 0; x < 2; ++x)
     for (int y = 0; y < 4; ++y)
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
-  const int boff = 32768 + ((lane * 8) & 4095);                 // < 36864
-  const int aoff = (lane & 31) * 4 + (lane >> 5) * 8192;        // < 8320
-  float a[2][8];
-  bf16x8_t ph[2], pl[2], b[4];
-  auto load = [&](int it) {
-    const int sw = (it & 7) << 4;
-    for (int nb = 0; nb < 4; ++nb) {
-      const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + (boff ^ sw) + nb * 1024));
-      const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + (boff ^ sw) + nb * 1024 + 2048));
-      b[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+  const int aoff = (lane * 8) & 511;      // A reads end below 512 + 127 + 3072 + 8
+  const int boff = 32768 + lane * 16;     // B reads end below 32768 + 1024 + 127 + 12288 + 16
+  f16x8_t a[2][2], b[2][4];
+  auto load = [&](int it, int h) {
+    const int sw = ((it * 2 + h) & 7) << 4;
     for (int mb = 0; mb < 2; ++mb) {
-      if constexpr (kPlanes) {
-        const int o = ((boff - 32768) ^ sw) + mb * 1024;
-        const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + o));
-        const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + o + 2048));
-        const i16x4_t l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + o + 16384));
-        const i16x4_t l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + o + 18432));
-        ph[mb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-        pl[mb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
-      } else {
-        for (int e = 0; e < 8; ++e) a[mb][e] = *(lds_f32*)((lds_u8*)lds + (aoff ^ sw) + mb * 128 + e * 1024);
-      }
+      const i16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + (aoff ^ sw) + mb * 1024));
+      const i16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + (aoff ^ sw) + mb * 1024 + 2048));
+      a[h][mb] = __builtin_bit_cast(f16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+    for (int nb = 0; nb < 4; ++nb)
+      b[h][nb] = *(lds_f16x8*)((lds_u8*)lds + (boff ^ sw) + nb * 4096);
   };
-  load(0);
+  load(0, 0);
+  load(0, 1);
   for (int it = 0; it < iters; ++it) {
-    bf16x8_t ah[2], al[2], bb[4];
-    for (int mb = 0; mb < 2; ++mb) {
-      if constexpr (kPlanes) {
-        ah[mb] = ph[mb];
-        al[mb] = pl[mb];
-      } else {
-        uint32_t h[4], l[4];
-        for (int e = 0; e < 4; ++e) split2(a[mb][2 * e], a[mb][2 * e + 1], h[e], l[e]);
-        ah[mb] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-        al[mb] = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-      }
+    for (int h = 0; h < 2; ++h) {
+      f16x8_t ah[2] = {a[h][0], a[h][1]}, bh[4] = {b[h][0], b[h][1], b[h][2], b[h][3]};
+      if constexpr (kReads) load(it + 1, h);
+      for (int mb = 0; mb < 2; ++mb)
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
     }
-    for (int nb = 0; nb < 4; ++nb) bb[nb] = b[nb];
-    load(it + 1);
-    for (int mb = 0; mb < 2; ++mb)
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bb[nb], acc[mb][nb], 0, 0, 0);
-    for (int mb = 0; mb < 2; ++mb)
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bb[nb], acc[mb][nb], 0, 0, 0);
   }
   float s = 0.f;
   for (int x = 0; x < 2; ++x)
@@ -304,16 +275,18 @@ int main() {
            b / (ms * 1e-3) / 256 / 2.1e9);
   }
 
-  printf("G_W inner loop alone (1 wave/SIMD, 64 x 128 per wave, 16 tokens per iteration):\n");
-  {
-    const int iters = 2048, wgs = 256;
+  printf("G_W inner loop alone (fp16, 64 x 128 per wave, 32 tokens per iteration):\n");
+  for (int wgs : {256, 512}) {
+    const int iters = 1024;
     const float ms0 = time_ms([](float* o, int g, int it) {
-      hipLaunchKernelGGL(gw_loop<false>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
+      hipLaunchKernelGGL(gw16_loop<true>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
     const float ms1 = time_ms([](float* o, int g, int it) {
-      hipLaunchKernelGGL(gw_loop<true>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
+      hipLaunchKernelGGL(gw16_loop<false>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
     const double fl = mfma_flops * 16.0 * iters * wgs * 4;
-    printf("  fp32 A, hi/lo split in the loop   %.3f ms  %7.1f TFLOP/s\n", ms0, fl / ms0 / 1e9);
-    printf("  bf16 hi/lo planes, no VALU        %.3f ms  %7.1f TFLOP/s\n", ms1, fl / ms1 / 1e9);
+    printf("  %d wave(s)/SIMD, LDS reads in the loop  %.3f ms  %7.1f TFLOP/s\n", wgs / 256, ms0,
+           fl / ms0 / 1e9);
+    printf("  %d wave(s)/SIMD, matrix work only       %.3f ms  %7.1f TFLOP/s\n", wgs / 256, ms1,
+           fl / ms1 / 1e9);
   }
   (void)hipFree(out);
   (void)hipFree(src);

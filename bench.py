@@ -37,6 +37,7 @@ METRIC = "token-draws/sec, LM-head Dust estimator (T=16384, V=4096) + % VALU/MFM
 # 157.3 TFLOP/s counted as FMAs.  fp16/bf16 dense MFMA 2.5 PFLOP/s.  HBM3E 8 TB/s.
 VALU_SLOTS_PER_S = 256 * 4 * 32 * 2.4e9
 FP16_MFMA_FLOPS = 2.5e15  # dense fp16 (and bf16) matrix cores
+SCAN_LAUNCHES = 50  # back-to-back reward scans timed for the scan's per-launch figure
 HBM_BYTES_PER_S = 8.0e12
 
 # VALU issue slots per normal (one column of one token-draw), charged at the
@@ -73,7 +74,8 @@ IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE = 25.5
 # they were taken on; they are reported only while the sources are unchanged.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "head_kernel_paper_traffic.json")
 KERNEL_SOURCES = ["activation_perturbation_estimator_amd/csrc/dust_head.hip",
-                  "activation_perturbation_estimator_amd/csrc/dust_device.hpp"]
+                  "activation_perturbation_estimator_amd/csrc/dust_device.hpp",
+                  "activation_perturbation_estimator_amd/csrc/dust_gemm16.hpp"]
 
 
 def kernel_source_hash() -> str:
@@ -323,10 +325,17 @@ def run_linear(args, torch, dust, synth, w):
     acc_bytes = 4.0 * w.K * w.T + 4.0 * w.T * w.V
     out["roofline"]["hbm_gbs"] = acc_bytes / (ee_ms / 1e3) / 1e9
     out["roofline"]["hbm_frac"] = acc_bytes / (ee_ms / 1e3) / HBM_BYTES_PER_S
-    out["reward_scan"] = {"bound": "hbm", "achieved": scan_bytes / (stage[0] / 1e3) / 1e9,
+    # the scan is ~10 us, so the stage events around it carry the launch gaps:
+    # its per-launch time comes from back-to-back calls between two events
+    rbuf = torch.empty((w.K, w.T), dtype=torch.float32, device=dev)
+    scan_ms = _time_calls(torch, lambda: dust.reward_scan(cd, seq_len=w.seq_len, gamma=w.gamma,
+                                                          out=rbuf), SCAN_LAUNCHES, 2)
+    del rbuf
+    out["reward_scan"] = {"bound": "hbm", "achieved": scan_bytes / (scan_ms / 1e3) / 1e9,
                           "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
-                          "frac": scan_bytes / (stage[0] / 1e3) / HBM_BYTES_PER_S,
-                          "launch_ms": stage[0]}
+                          "frac": scan_bytes / (scan_ms / 1e3) / HBM_BYTES_PER_S,
+                          "launch_ms": scan_ms, "launches": SCAN_LAUNCHES,
+                          "stage_ms": stage[0]}
     out["stages_ms"] = {"reward_scan": stage[0], "error_estimate": stage[1], "outer_sum": stage[2]}
     out["outer_sum"] = outer_sum_fields(w, stage[2])
     if not args.no_cpu_baseline:
