@@ -27,16 +27,18 @@
 // the buffer's bounds check covers all of it: loads past a token split's rows
 // return zeros.
 //
-// Tiling: a workgroup (4 waves, one per SIMD) owns a 2 kWM x 256 tile of G over
-// one token range (split-K over tokens so that the grid fills the 256 CUs);
-// each wave owns kWM x 128 as kWM/32 x 4 MFMA blocks.  Partial tiles of the
-// token splits are summed in a fixed order by a second kernel, so results are
-// deterministic.
+// Tiling: a workgroup of kWavesM x kWavesN waves owns a kWavesM kWM x kWavesN kWN
+// tile of G over one token range (split-K over tokens so that the grid fills
+// the 256 CUs); each wave owns kWM x kWN as kWM/32 x kWN/32 MFMA blocks.  The
+// built configuration: 8 waves (two per SIMD) of 64 x 128 on a 256 x 256 tile,
+// 32 tokens per pipeline step, a ring of 4 steps (128 KiB of LDS).  Partial
+// tiles of the token splits are summed in a fixed order by a second kernel, so
+// results are deterministic.
 #include "dust_device.hpp"
 #include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
 
-// Tile shape of the G_W kernel (see Cfg below): 0 is the built configuration;
+// Tile shape of the G_W kernel (see Cfg below): 1 is the built configuration;
 // the others are kept for measurement on other shapes and parts.
 #ifndef DUST_GEMM_CONFIG
 #define DUST_GEMM_CONFIG 1

@@ -33,12 +33,27 @@
  *     input width, K draws.
  *   - Size limits (DUST_ERR_UNSUPPORTED beyond them): the calls that form G_W
  *     take T <= 2^22 and N, d <= 2^20, with at most 2^24 - 1 workgroups in the
- *     outer-product grid: ceil(N/128) x ceil(d/256) tiles of G_W times the
- *     token splits, where one split holds at most about 2^29 / (max(N, d/2) + 128)
- *     tokens (at T = 2^22 this binds from N = d = 2^16 up); the per-token
- *     stages (dust_head_losses, dust_centre, dust_error_estimate,
+ *     outer-product grid: ceil(N/256) x ceil(d/256) tiles of G_W times the
+ *     token splits (the splits x row tiles rounded up to a multiple of 8),
+ *     where one split holds at most about 2^30 / (max(N, d) + 256) tokens;
+ *     the per-token stages (dust_head_losses, dust_centre, dust_error_estimate,
  *     dust_perturbed_linear, dust_ce_grad) take T < 2^24; element counts of
  *     every array stay <= 2^40.
+ *   - G_W precision (every call that forms G_W): the product runs on the fp16
+ *     matrix cores with fp32 accumulation, over copies of each token's g_t and
+ *     x_t rescaled by 2^-s_t and 2^s_t (exact; s_t from the two rows' maxima)
+ *     and rounded to fp16.  Each product g x then errs by at most 2^-11 of
+ *     itself (2^-10 with fp32 X), except elements that fall below fp16's normal
+ *     range after scaling (below 2^-14: from 2^-3 of their row's maximum when
+ *     the two maxima's exponents sum to -22, the lowest admitted, to 2^-27 at
+ *     the highest, 26), which keep an absolute error of 2^-25.  Tokens whose
+ *     maxima fit no power of two, or with a non-finite value, are added in
+ *     fp32 from the original rows.  Results are deterministic.
+ *   - Support calls are this library's own conventions, not steps of the
+ *     method, and cite no passage: dust_status_string, dust_version, the
+ *     *_workspace_size and dust_embedding_noalloc_bytes size queries,
+ *     dust_philox4x32_10 (the raw generator behind the noise convention
+ *     below, for checking it) and dust_check_targets (an opt-in input check).
  *
  * Noise convention (the pages fix only that the noise is standard normal and
  * independent per token; this is this library's counter-based stream, which
