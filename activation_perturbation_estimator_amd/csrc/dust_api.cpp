@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstring>
 
 #include "dust.h"
 #include "dust_launch.hpp"
@@ -24,7 +25,21 @@ bool sigma_ok(float sigma) {
   return std::isfinite(sigma) && sigma > 0.f && sigma <= DUST_SIGMA_MAX;
 }
 bool gamma_ok(float gamma) { return std::isfinite(gamma) && gamma >= 0.f && gamma <= 1.f; }
-bool dtype_ok(dust_dtype dt) { return dt == DUST_F32 || dt == DUST_BF16; }
+// Enum arguments come from C callers, who may pass any int; in C++ loading an
+// enum object whose value lies outside its enumerators' range is undefined, so
+// the value is read from the object's bytes as an int before it is checked.
+static_assert(sizeof(dust_dtype) == sizeof(int) && sizeof(dust_status) == sizeof(int),
+              "the ABI's enums are passed as int");
+template <typename E>
+int enum_value(const E& e) {
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool dtype_ok(const dust_dtype& dt) {
+  const int v = enum_value(dt);
+  return v == DUST_F32 || v == DUST_BF16;
+}
 
 // Index products stay far below 2^62, the 32-bit counter words hold t and i,
 // token positions of the G_W and embedding calls fit int32, and the kernels
@@ -35,13 +50,15 @@ constexpr int64_t kMaxWidth = (int64_t)1 << 20;      // N and d of the calls tha
 constexpr int64_t kMaxTokens = ((int64_t)1 << 24) - 1;  // the other per-token calls
 constexpr int64_t kMaxK = ((int64_t)1 << 31) - 64;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kMaxVocab = (int64_t)1 << 24;      // the embedding calls
 
 bool width_ok(int64_t N) { return N > 0 && N % 4 == 0 && N <= DUST_N_MAX; }
 
 // A range of draws draw0 .. draw0 + K - 1 of a population of K_total: the
 // draw is a 32-bit counter word of the noise.
 bool draws_ok(int64_t draw0, int64_t K, int64_t K_total) {
-  return draw0 >= 0 && K_total >= 1 && K_total <= kMaxK && draw0 <= ((int64_t)1 << 32) - K;
+  return draw0 >= 0 && K >= 0 && K <= kMaxK && K_total >= 1 && K_total <= kMaxK &&
+         draw0 <= ((int64_t)1 << 32) - K;
 }
 
 // a * b <= lim for a, b >= 0, without forming a product that could overflow.
@@ -98,7 +115,7 @@ void* aligned_base(void* ws) {
 extern "C" {
 
 const char* dust_status_string(dust_status st) {
-  switch (st) {
+  switch (enum_value(st)) {
     case DUST_OK: return "DUST_OK";
     case DUST_ERR_INVALID_ARG: return "DUST_ERR_INVALID_ARG";
     case DUST_ERR_WORKSPACE: return "DUST_ERR_WORKSPACE";
@@ -111,18 +128,23 @@ const char* dust_status_string(dust_status st) {
 
 const char* dust_version(void) { return "libdust 1.0 gfx950"; }
 
+// The size queries answer the minimum for sizes the calls reject (invalid, or
+// beyond the size limits), so that no size arithmetic runs on them.
 size_t dust_head_workspace_size(int64_t T, int64_t V, int64_t d, int64_t K, float gamma) {
   if (T < 0 || V <= 0 || d <= 0 || K <= 0) return kAlign;
+  if (T > kMaxT || V > kMaxWidth || d > kMaxWidth || K > kMaxK) return kAlign;
   return head_plan(T, V, d, K, gamma).total();
 }
 
 size_t dust_linear_workspace_size(int64_t T, int64_t d_in, int64_t N, int64_t K, float gamma) {
   if (T < 0 || N <= 0 || d_in <= 0 || K <= 0) return kAlign;
+  if (T > kMaxT || N > kMaxWidth || d_in > kMaxWidth || K > kMaxK) return kAlign;
   return linear_plan(T, d_in, N, K, gamma).total();
 }
 
 size_t dust_outer_sum_workspace_size(int64_t T, int64_t N, int64_t d) {
   if (T < 0 || N <= 0 || d <= 0) return kAlign;
+  if (T > kMaxT || N > kMaxWidth || d > kMaxWidth) return kAlign;
   return align_up(dust::outer_sum_workspace_bytes(T, N, d)) + kAlign;
 }
 
@@ -224,7 +246,7 @@ dust_status dust_linear_estimate(const void* X, dust_dtype x_dt, const float* c,
 dust_status dust_noise(uint64_t seed, uint32_t stream, int64_t draw0, int64_t ndraw, int64_t T,
                        int64_t N, float* out, dust_stream_t s) {
   if (!out || ndraw < 0 || T < 0 || !width_ok(N) || draw0 < 0) return DUST_ERR_INVALID_ARG;
-  if (draw0 + ndraw > ((int64_t)1 << 32) || T > ((int64_t)1 << 32)) return DUST_ERR_INVALID_ARG;
+  if (draw0 > ((int64_t)1 << 32) - ndraw || T > ((int64_t)1 << 32)) return DUST_ERR_INVALID_ARG;
   if (!prod_le(ndraw, T, kMaxElems / N)) return DUST_ERR_UNSUPPORTED;
   return hip_status(dust::launch_noise_fill(out, ndraw, T, N, (uint32_t)draw0, stream, seed,
                                             as_stream(s)));
@@ -297,7 +319,7 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
   if (T <= 0 || N <= 0 || N % 4 != 0 || d <= 0 || d % 8 != 0) return DUST_ERR_INVALID_ARG;
   if (T > kMaxTokens || N > kMaxWidth || d > kMaxWidth) return DUST_ERR_UNSUPPORTED;
   if (!dust::perturbed_linear_supported(T, N)) return DUST_ERR_UNSUPPORTED;
-  if (!sigma_ok(sigma) || draw0 < 0 || ndraw < 0 || draw0 + ndraw > ((int64_t)1 << 32))
+  if (!sigma_ok(sigma) || draw0 < 0 || ndraw < 0 || draw0 > ((int64_t)1 << 32) - ndraw)
     return DUST_ERR_INVALID_ARG;
   if (ndraw * T > kMaxElems / N) return DUST_ERR_UNSUPPORTED;
   // the operand windows of one 128-row tile stay inside 32-bit byte offsets
@@ -309,6 +331,7 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
 
 size_t dust_embedding_workspace_size(int64_t T, int64_t N, int64_t vocab) {
   if (T < 0 || N <= 0 || vocab <= 0) return kAlign;
+  if (T > kMaxT || N > kMaxWidth || vocab > kMaxVocab) return kAlign;
   return dust::embedding_workspace_bytes(T, N, vocab) + kAlign;
 }
 
@@ -317,7 +340,7 @@ dust_status dust_embedding_grad(const int32_t* ids, const float* g_hat, int64_t 
                                 size_t workspace_bytes, dust_stream_t s) {
   if (!ids || !g_hat || !G_E || T < 0 || N <= 0 || N % 4 != 0 || vocab <= 0)
     return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT || N > kMaxWidth || vocab > ((int64_t)1 << 24) || T * N > kMaxElems ||
+  if (T > kMaxT || N > kMaxWidth || vocab > kMaxVocab || T * N > kMaxElems ||
       vocab * N > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
   if (((T + 511) / 512) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
@@ -331,7 +354,7 @@ dust_status dust_embedding_grad_noalloc(const int32_t* ids, const float* g_hat, 
                                         int64_t N, int64_t vocab, float* G_E, dust_stream_t s) {
   if (!ids || !g_hat || !G_E || T < 0 || N <= 0 || N % 4 != 0 || vocab <= 0)
     return DUST_ERR_INVALID_ARG;
-  if (T > kMaxT || N > kMaxWidth || vocab > ((int64_t)1 << 24) || T * N > kMaxElems ||
+  if (T > kMaxT || N > kMaxWidth || vocab > kMaxVocab || T * N > kMaxElems ||
       vocab * N > kMaxElems)
     return DUST_ERR_UNSUPPORTED;
   if (((T + 511) / 512) * vocab > ((int64_t)1 << 31)) return DUST_ERR_UNSUPPORTED;
@@ -345,12 +368,14 @@ dust_status dust_embedding_grad_noalloc(const int32_t* ids, const float* g_hat, 
 
 size_t dust_embedding_noalloc_bytes(int64_t T, int64_t N, int64_t vocab) {
   if (T < 0 || N <= 0 || vocab <= 0) return 0;
+  if (T > kMaxT || N > kMaxWidth || vocab > kMaxVocab) return 0;
   return dust::embedding_workspace_bytes(T, N, vocab);
 }
 
 dust_status dust_sgd_momentum(float* W, const float* G, float* m, int64_t n, float lr,
                               float momentum, float weight_decay, dust_stream_t s) {
   if (n < 0 || (n > 0 && (!W || !G || !m))) return DUST_ERR_INVALID_ARG;
+  if (n > kMaxElems) return DUST_ERR_UNSUPPORTED;
   if (!std::isfinite(lr) || !std::isfinite(momentum) || !std::isfinite(weight_decay))
     return DUST_ERR_INVALID_ARG;
   return hip_status(dust::launch_sgd_momentum(W, G, m, n, lr, momentum, weight_decay,
@@ -361,6 +386,7 @@ dust_status dust_adam(float* W, const float* G, float* m, float* v, int64_t n, f
                       float beta1, float beta2, float eps, float weight_decay, int64_t step,
                       dust_stream_t s) {
   if (n < 0 || (n > 0 && (!W || !G || !m || !v)) || step < 1) return DUST_ERR_INVALID_ARG;
+  if (n > kMaxElems) return DUST_ERR_UNSUPPORTED;
   if (!std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) ||
       !(eps > 0.f) || !std::isfinite(eps) || !std::isfinite(weight_decay))
     return DUST_ERR_INVALID_ARG;

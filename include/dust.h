@@ -144,7 +144,9 @@ dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt,
                                void* workspace, size_t workspace_bytes,
                                dust_stream_t s, const dust_event_t* stage_events);
 
-/* Bytes of workspace dust_head_estimate needs (0 is never returned). */
+/* Bytes of workspace dust_head_estimate needs (0 is never returned; for sizes
+ * the call rejects, invalid or beyond the size limits, the minimum of 256).
+ * The other *_workspace_size queries answer the same way. */
 size_t dust_head_workspace_size(int64_t T, int64_t V, int64_t d, int64_t K, float gamma);
 
 /* Hidden linear layer y = W x (paper digest, section 2.2): the caller ran its
@@ -275,7 +277,8 @@ size_t dust_embedding_workspace_size(int64_t T, int64_t N, int64_t vocab);
 #define DUST_EMBEDDING_NOALLOC_BYTES ((size_t)16 << 20)
 dust_status dust_embedding_grad_noalloc(const int32_t* ids, const float* g_hat, int64_t T,
                                         int64_t N, int64_t vocab, float* G_E, dust_stream_t s);
-/* Scratch bytes dust_embedding_grad_noalloc needs for a size (0 for invalid sizes). */
+/* Scratch bytes dust_embedding_grad_noalloc needs for a size (0 for invalid
+ * sizes and sizes beyond dust_embedding_grad's limits). */
 size_t dust_embedding_noalloc_bytes(int64_t T, int64_t N, int64_t vocab);
 
 /* Optimiser steps on a weight gradient (linlog explainer, experiment setup:
@@ -283,7 +286,8 @@ size_t dust_embedding_noalloc_bytes(int64_t T, int64_t N, int64_t vocab);
  * [n], updated in place; G_W approximates +dL/dW, so W moves against it.
  *   SGD:  m = momentum m + (G + wd W);  W -= lr m   (PyTorch SGD, dampening 0)
  *   Adam: g = G + wd W; m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
- *         W -= lr/(1-b1^step) m / (sqrt(v)/sqrt(1-b2^step) + eps)  (step >= 1) */
+ *         W -= lr/(1-b1^step) m / (sqrt(v)/sqrt(1-b2^step) + eps)  (step >= 1)
+ * n <= 2^40 (DUST_ERR_UNSUPPORTED beyond). */
 dust_status dust_sgd_momentum(float* W, const float* G, float* m, int64_t n, float lr,
                               float momentum, float weight_decay, dust_stream_t s);
 dust_status dust_adam(float* W, const float* G, float* m, float* v, int64_t n, float lr,

@@ -53,9 +53,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    # DUST_ORACLE_LIB names another build of dust_oracle.c to load as it is
+    # (the test suite's sanitizer build); by default the file next to the source.
+    path = os.environ.get("DUST_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     lib.oracle_philox_batch.argtypes = [_u64, _u32p, _u32p, _i64]
     lib.oracle_philox_batch.restype = None
     lib.oracle_uniform_batch.argtypes = [_u32p, _f64p, _i64]
