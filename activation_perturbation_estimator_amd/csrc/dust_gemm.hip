@@ -30,19 +30,15 @@
 // Tiling: a workgroup of kWavesM x kWavesN waves owns a kWavesM kWM x kWavesN kWN
 // tile of G over one token range (split-K over tokens so that the grid fills
 // the 256 CUs); each wave owns kWM x kWN as kWM/32 x kWN/32 MFMA blocks.  The
-// built configuration: 8 waves (two per SIMD) of 64 x 128 on a 256 x 256 tile,
-// 32 tokens per pipeline step, a ring of 4 steps (128 KiB of LDS).  Partial
-// tiles of the token splits are summed in a fixed order by a second kernel, so
-// results are deterministic.
+// built configurations (WideCfg, NarrowCfg below): waves of 64 x 128 on
+// 256 x 256 or 256 x 128 tiles, 32 tokens per pipeline step, a ring of 4
+// steps (128 or 96 KiB of LDS).  Partial tiles of the token splits are summed
+// in a fixed order by a second kernel, so results are deterministic.
+#include <type_traits>
+
 #include "dust_device.hpp"
 #include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
-
-// Tile shape of the G_W kernel (see Cfg below): 1 is the built configuration;
-// the others are kept for measurement on other shapes and parts.
-#ifndef DUST_GEMM_CONFIG
-#define DUST_GEMM_CONFIG 1
-#endif
 
 namespace dust {
 
@@ -86,23 +82,13 @@ struct Cfg {
   static_assert(kS * kStage <= 160 * 1024, "LDS of one CU");
 };
 
-#if DUST_GEMM_CONFIG == 0
-using GemmCfg = Cfg<2, 2, 128, 128, 32, 4>;
-#elif DUST_GEMM_CONFIG == 1
-using GemmCfg = Cfg<4, 2, 64, 128, 32, 4>;
-#elif DUST_GEMM_CONFIG == 2
-using GemmCfg = Cfg<2, 2, 64, 128, 32, 4>;
-#elif DUST_GEMM_CONFIG == 3
-using GemmCfg = Cfg<2, 2, 64, 128, 64, 3>;
-#elif DUST_GEMM_CONFIG == 4
-using GemmCfg = Cfg<4, 2, 32, 128, 32, 4>;
-#elif DUST_GEMM_CONFIG == 5
-using GemmCfg = Cfg<4, 2, 64, 128, 64, 2>;
-#elif DUST_GEMM_CONFIG == 6
-using GemmCfg = Cfg<2, 2, 128, 128, 64, 2>;
-#elif DUST_GEMM_CONFIG == 7
-using GemmCfg = Cfg<4, 2, 32, 128, 64, 3>;
-#endif
+// Two tile shapes, chosen per call (plan16): 256 x 256 tiles (8 waves, two per
+// SIMD, of 64 x 128) fill the chip with at most 8 token splits when the
+// output has at least 32 such tiles (N d >= 2^21); smaller outputs take
+// 256 x 128 tiles (4 waves of 64 x 128), which need half the splits and so
+// half the partial bytes.
+using WideCfg = Cfg<4, 2, 64, 128, 32, 4>;
+using NarrowCfg = Cfg<4, 1, 64, 128, 32, 4>;
 
 // s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
@@ -165,6 +151,7 @@ __global__ void __launch_bounds__(256) prep16_kernel(const float* __restrict__ g
 struct Gemm16Geom {
   int64_t M, Mp, d, T, tiles_m, tiles_n, nsplit, t_per_split, groups, groups_per_xcd;
   int64_t pstride;  // elements between the partial tiles of consecutive splits
+  int wide;         // WideCfg (1) or NarrowCfg (0)
 };
 
 template <typename C>
@@ -503,8 +490,8 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
   }
 }
 
-static Gemm16Geom plan16(int64_t T, int64_t M, int64_t d) {
-  using C = GemmCfg;
+template <typename C>
+static Gemm16Geom plan16_t(int64_t T, int64_t M, int64_t d) {
   Gemm16Geom g;
   g.M = M;
   g.Mp = (M + 7) / 8 * 8;
@@ -522,11 +509,16 @@ static Gemm16Geom plan16(int64_t T, int64_t M, int64_t d) {
   int64_t per = (T + ns - 1) / ns;
   constexpr int64_t gran = C::kS * C::kBT;  // whole ring turns per split
   per = (per + gran - 1) / gran * gran;
-  // 32-bit buffer offsets: a split's rows of g16 (and token groups of x16),
-  // plus one ring turn of prefetch past them, stay below 2^31 bytes.
-  const int64_t rb_g = 2 * (g.Mp + C::kBM), rb_x = 2 * (d + C::kBN);
-  const int64_t row_bytes = rb_g > rb_x ? rb_g : rb_x;
-  const int64_t per_max = ((((int64_t)1 << 31) - 1) / row_bytes - 3 * gran) / gran * gran;
+  // 32-bit buffer offsets: over a split's rows of g16 and token groups of
+  // x16, plus the three ring steps of prefetch past them and the column
+  // overrun of the last tile (one row of g16, one group of x16), every offset
+  // stays below 2^31 bytes: 2 W (per + 3 gran) + o (W + tile width) < 2^31,
+  // W = Mp and o = 2 for g16, W = d and o = 16 for x16.
+  auto per_limit = [&](int64_t W, int64_t B, int64_t o) {
+    return ((((int64_t)1 << 31) - 1 - o * (W + B)) / (2 * W) - 3 * gran) / gran * gran;
+  };
+  const int64_t lim_g = per_limit(g.Mp, C::kBM, 2), lim_x = per_limit(d, C::kBN, 16);
+  const int64_t per_max = lim_g < lim_x ? lim_g : lim_x;
   if (per > per_max) per = per_max > gran ? per_max : gran;
   g.t_per_split = per > 0 ? per : gran;
   g.nsplit = (T + g.t_per_split - 1) / g.t_per_split;
@@ -534,7 +526,13 @@ static Gemm16Geom plan16(int64_t T, int64_t M, int64_t d) {
   g.groups = g.tiles_m * g.nsplit;
   g.groups_per_xcd = (g.groups + kXcds - 1) / kXcds;
   g.pstride = (M * d + 63) / 64 * 64;
+  g.wide = std::is_same<C, WideCfg>::value ? 1 : 0;
   return g;
+}
+
+static Gemm16Geom plan16(int64_t T, int64_t M, int64_t d) {
+  const Gemm16Geom w = plan16_t<WideCfg>(T, M, d);
+  return w.nsplit <= 8 ? w : plan16_t<NarrowCfg>(T, M, d);
 }
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -593,8 +591,12 @@ hipError_t launch_outer_sum16(const Gemm16Out& o, const float* g32, int64_t N, f
   int32_t* count = reinterpret_cast<int32_t*>(ws + w.list);
   float* part = reinterpret_cast<float*>(ws + w.list + w.count);
   const int64_t nwg = geo.groups_per_xcd * kXcds * geo.tiles_n;
-  hipLaunchKernelGGL(gemm16_kernel<GemmCfg>, dim3((uint32_t)nwg), dim3(GemmCfg::kThreads), 0, s,
-                     o.g16, o.x16, o.flags, geo, part, list, count);
+  if (geo.wide)
+    hipLaunchKernelGGL(gemm16_kernel<WideCfg>, dim3((uint32_t)nwg), dim3(WideCfg::kThreads), 0, s,
+                       o.g16, o.x16, o.flags, geo, part, list, count);
+  else
+    hipLaunchKernelGGL(gemm16_kernel<NarrowCfg>, dim3((uint32_t)nwg), dim3(NarrowCfg::kThreads), 0,
+                       s, o.g16, o.x16, o.flags, geo, part, list, count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = N * o.d;

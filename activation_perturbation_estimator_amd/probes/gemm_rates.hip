@@ -20,6 +20,21 @@ typedef __attribute__((address_space(3))) f32x2_t lds_f32x2;
 typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
+// Clock of each workgroup's run: shader-clock ticks (s_memtime) and
+// constant-rate ticks (s_memrealtime) between its first and last instruction,
+// recorded by thread 0 of workgroups below 1024.
+__device__ unsigned long long g_clk[1024 * 2];
+struct ClockSpan {
+  long long c0, w0;
+  __device__ ClockSpan() : c0(clock64()), w0(wall_clock64()) {}
+  __device__ void record() const {
+    if (threadIdx.x == 0 && blockIdx.x < 1024) {
+      g_clk[2 * blockIdx.x] = (unsigned long long)(clock64() - c0);
+      g_clk[2 * blockIdx.x + 1] = (unsigned long long)(wall_clock64() - w0);
+    }
+  }
+};
+
 // 1. Matrix cores alone: 16 independent v_mfma_f32_32x32x16_bf16 per iteration.
 __global__ void __launch_bounds__(256) mfma_only(float* out, int iters) {
   const int lane = threadIdx.x & 63;
@@ -51,6 +66,7 @@ __global__ void __launch_bounds__(256) mfma_only(float* out, int iters) {
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 template <bool kF16, int kBlocks>
 __global__ void __launch_bounds__(256, 1) mfma_rate(float* out, int iters) {
+  const ClockSpan span;
   const int lane = threadIdx.x & 63;
   f16x8_t ah[4], bh[4];
   bf16x8_t ab[4], bb[4];
@@ -77,6 +93,7 @@ __global__ void __launch_bounds__(256, 1) mfma_rate(float* out, int iters) {
   for (int x = 0; x < kBlocks; ++x)
     for (int r = 0; r < 16; ++r) s += acc[x][r];
   out[blockIdx.x * 256 + threadIdx.x] = s;
+  span.record();
 }
 
 // 2. LDS reads: 8 reads per iteration of one form, addresses moving with the
@@ -150,6 +167,7 @@ __global__ void __launch_bounds__(256) lds_dma(const float* src, float* out, int
 typedef __attribute__((address_space(3))) f16x8_t lds_f16x8;
 template <bool kReads>
 __global__ void __launch_bounds__(256) gw16_loop(float* out, int iters) {
+  const ClockSpan span;
   __shared__ __attribute__((aligned(16))) unsigned char lds[65536];
   for (int i = threadIdx.x; i < 16384; i += 256) reinterpret_cast<float*>(lds)[i] = 0.001f * (i & 7);
   __syncthreads();
@@ -187,6 +205,20 @@ __global__ void __launch_bounds__(256) gw16_loop(float* out, int iters) {
     for (int y = 0; y < 4; ++y)
       for (int r = 0; r < 16; ++r) s += acc[x][y][r];
   out[blockIdx.x * 256 + threadIdx.x] = s;
+  span.record();
+}
+
+// Shader clock of the last timed launch, from the spans of its first `wgs`
+// workgroups (at most 1024): s_memtime ticks over s_memrealtime time.
+static double span_ghz(int wgs, double realtime_hz) {
+  static unsigned long long h[1024 * 2];
+  if (hipMemcpyFromSymbol(h, HIP_SYMBOL(g_clk), sizeof(h)) != hipSuccess) return 0.0;
+  double c = 0.0, w = 0.0;
+  for (int b = 0; b < wgs && b < 1024; ++b) {
+    c += (double)h[2 * b];
+    w += (double)h[2 * b + 1];
+  }
+  return w > 0.0 ? c / (w / realtime_hz) / 1e9 : 0.0;
 }
 
 static float time_ms(void (*launch)(float*, int, int), float* out, int wgs, int iters) {
@@ -216,6 +248,10 @@ int main() {
   (void)hipMemset(src, 0, 1 << 20);
   g_src = src;
   const double mfma_flops = 2.0 * 32 * 32 * 16;  // per v_mfma_f32_32x32x16_bf16
+  int rt_khz = 0;
+  if (hipDeviceGetAttribute(&rt_khz, hipDeviceAttributeWallClockRate, 0) != hipSuccess || rt_khz <= 0)
+    rt_khz = 100000;
+  const double rt_hz = rt_khz * 1e3;
 
   printf("bf16 MFMA (v_mfma_f32_32x32x16_bf16), 16 independent per iteration:\n");
   for (int wgs : {256, 512, 1024}) {
@@ -240,8 +276,9 @@ int main() {
         default: ms = time_ms([](float* o, int g, int it) { hipLaunchKernelGGL((mfma_rate<true, 16>), dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters); break;
       }
       const double fl = mfma_flops * 32.0 * iters * wgs * 4;
-      printf("  %s  %.3f ms  %7.1f TFLOP/s  (%.2f GHz at 32 cycles per MFMA)\n", nm[v], ms,
-             fl / ms / 1e9, 32.0 * iters * wgs * 4 / 1024 * 32 / (ms * 1e-3) / 1e9);
+      printf("  %s  %.3f ms  %7.1f TFLOP/s  (%.2f GHz at 32 cycles per MFMA; s_memtime %.2f GHz)\n",
+             nm[v], ms, fl / ms / 1e9, 32.0 * iters * wgs * 4 / 1024 * 32 / (ms * 1e-3) / 1e9,
+             span_ghz(wgs, rt_hz));
     }
   }
 
@@ -280,13 +317,15 @@ int main() {
     const int iters = 1024;
     const float ms0 = time_ms([](float* o, int g, int it) {
       hipLaunchKernelGGL(gw16_loop<true>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
+    const double ghz0 = span_ghz(wgs, rt_hz);
     const float ms1 = time_ms([](float* o, int g, int it) {
       hipLaunchKernelGGL(gw16_loop<false>, dim3(g), dim3(256), 0, 0, o, it); }, out, wgs, iters);
+    const double ghz1 = span_ghz(wgs, rt_hz);
     const double fl = mfma_flops * 16.0 * iters * wgs * 4;
-    printf("  %d wave(s)/SIMD, LDS reads in the loop  %.3f ms  %7.1f TFLOP/s\n", wgs / 256, ms0,
-           fl / ms0 / 1e9);
-    printf("  %d wave(s)/SIMD, matrix work only       %.3f ms  %7.1f TFLOP/s\n", wgs / 256, ms1,
-           fl / ms1 / 1e9);
+    printf("  %d wave(s)/SIMD, LDS reads in the loop  %.3f ms  %7.1f TFLOP/s  (s_memtime %.2f GHz)\n",
+           wgs / 256, ms0, fl / ms0 / 1e9, ghz0);
+    printf("  %d wave(s)/SIMD, matrix work only       %.3f ms  %7.1f TFLOP/s  (s_memtime %.2f GHz)\n",
+           wgs / 256, ms1, fl / ms1 / 1e9, ghz1);
   }
   (void)hipFree(out);
   (void)hipFree(src);

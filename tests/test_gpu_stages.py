@@ -171,9 +171,10 @@ def test_check_targets():
     assert not dust.check_targets(y, 100)
 
 
-def test_reward_scan_more_jobs_than_grid():
-    """K * T / L = 524288 (draw, sequence) jobs: more than the scan's grid of
-    65536 workgroups x 4 waves, so every wave walks several jobs."""
+def test_reward_scan_many_short_segments():
+    """K * T / L = 524288 (draw, sequence) segments of 2 tokens: a tile of the
+    scan holds 1024 whole segments, so nearly every thread's elements span a
+    segment end."""
     dust = need_gpu()
     import torch
     K, T, L = 4096, 256, 2
