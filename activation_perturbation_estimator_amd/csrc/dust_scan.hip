@@ -30,32 +30,72 @@ __global__ void __launch_bounds__(256) centre_kernel(const float* x, int64_t K, 
 // Segmented reverse scan r_t = c_t + gamma r_{t+1} (r = c at a segment's last
 // token) over the flattened [K,T] array, whose segments are its runs of L
 // consecutive elements.  One workgroup of 256 threads scans a tile of up to
-// 2048 elements, 8 consecutive ones per thread:
-//   - L <= 2048: a tile is m = floor(2048/L) whole segments (the tile's last
+// 8192 elements, 32 consecutive ones (a chunk) per thread:
+//   - L <= 8192: a tile is m = floor(8192/L) whole segments (the tile's last
 //     element ends a segment, so nothing flows in from the right);
-//   - L > 2048: a workgroup walks one segment in tiles from its end, carrying
+//   - L > 8192: a workgroup walks one segment in tiles from its end, carrying
 //     r of each tile's first element into the tile to its left.
-// Per tile: coalesced loads into LDS; each thread reduces its 8 elements to an
-// affine map r_first = A + B r_after (B = 0 when a segment ends inside them); a
-// suffix scan of the maps, by shuffles inside each wave and through LDS
-// across the four waves, gives every thread the r that follows its elements;
-// a second pass over the 8 elements writes r to LDS; coalesced stores.  The
-// whole tile is read before any of it is written, so r may be c.
+// Per tile: coalesced loads; each thread reduces its chunk to an affine map
+// r_first = A + B r_after (B = 0 when a segment ends inside it); a suffix scan
+// of the maps (inside each wave by DPP lane shifts, across the 4 waves through
+// LDS) gives every thread the r that follows its chunk; a second pass over the
+// chunk writes r; stores.  The whole tile is read before any of it is written,
+// so r may be c.  Long chunks keep the wave count low: waves start at a few
+// thousand per microsecond, and with 8 elements per thread the 32 MiB of the
+// hidden-layer workload spent as long starting waves (and waiting at the
+// barrier for a workgroup's last ones) as moving data.
 // gamma^m underflows to 0 in fp32 for long distances (0.9^2048): harmless.
 constexpr int kScanThreads = 256;
-constexpr int kScanE = 8;
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanE = 32;
 constexpr int kScanTile = kScanThreads * kScanE;
 
+// Maps compose as (A, B) o (A', B') = (A + B A', B B'): the left one is applied
+// after the right one.  compose_dpp<ctrl, rows>: each lane of the enabled rows
+// takes the map of the lane the DPP control names (the identity (0, 1) where
+// there is none) and composes it on the right of its own.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void compose_dpp(float& A, float& B) {
+  const float Ap = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(A), kCtrl, kRowMask,
+                                                              0xf, false));
+  const float Bp = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f),
+                                                              __float_as_int(B), kCtrl, kRowMask,
+                                                              0xf, false));
+  A = fmaf(B, Ap, A);
+  B *= Bp;
+}
+
+// Inclusive scan of the maps over the lanes of a wave, lane 0 first: lane l
+// ends with f_l o f_(l-1) o ... o f_0.  Shifts by 1, 2, 4 and 8 lanes inside
+// each row of 16, then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ void wave_scan_maps(float& A, float& B) {
+  compose_dpp<0x111, 0xf>(A, B);  // row_shr:1
+  compose_dpp<0x112, 0xf>(A, B);  // row_shr:2
+  compose_dpp<0x114, 0xf>(A, B);  // row_shr:4
+  compose_dpp<0x118, 0xf>(A, B);  // row_shr:8
+  compose_dpp<0x142, 0xa>(A, B);  // row_bcast:15
+  compose_dpp<0x143, 0xc>(A, B);  // row_bcast:31
+}
+
+// Tiles go through LDS, chunk by chunk ([chunk][36] floats: 16-byte aligned
+// rows whose starts fall on different banks for the 16 lanes of a read
+// phase), so that the global loads and stores stay coalesced.
 // kVec: every tile starts at a multiple of 4 elements of 16-byte aligned
-// arrays (L % 4 == 0), so each thread moves its 8 elements with two 16-byte
-// loads and stores of its own, without the LDS staging.
-template <bool kVec>
+// arrays (L % 4 == 0), and its global accesses are 16 bytes per lane.
+// P: the integer type of positions within a segment (int32_t when L < 2^30).
+template <bool kVec, typename P>
 __global__ void __launch_bounds__(kScanThreads) reward_scan_kernel(const float* c, int64_t nseg,
                                                                    int64_t L, float gamma,
                                                                    float* r) {
-  __shared__ float buf[kVec ? 1 : kScanThreads * (kScanE + 1)];
-  __shared__ float wa[4], wb[4], tile_carry;
+  constexpr int kRow = kScanE + 4;
+  __shared__ __attribute__((aligned(16))) float buf[kScanThreads * kRow];
+  __shared__ float wa[kScanWaves], wb[kScanWaves], tile_carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave's chunks run right to left over its lanes, so that the suffix
+  // scan over the wave's chunks is a prefix scan over its lanes.
+  const int q = wave * 64 + (63 - lane);  // this thread's chunk of the tile
+  const int j0 = q * kScanE;
   const bool long_seg = L > kScanTile;
   const int64_t m = long_seg ? 1 : kScanTile / L;  // segments per tile
   const int64_t njobs = (nseg + m - 1) / m;
@@ -64,38 +104,40 @@ __global__ void __launch_bounds__(kScanThreads) reward_scan_kernel(const float* 
   // segment unless carry_in flows from a tile to its right.  The element at
   // local index j ends a segment when (pos0 + j) % L == L - 1.
   auto scan_tile = [&](int64_t base, int n, int64_t pos0, float carry_in) -> float {
-    const int j0 = tid * kScanE;
     float xv[kScanE];
-    if constexpr (kVec) {
-      // n is a multiple of 4: each half of the thread's 8 is wholly in or out
+    if constexpr (kVec) {  // n is a multiple of 4
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j0 + 4 * h < n) v = *reinterpret_cast<const float4*>(c + base + j0 + 4 * h);
-        xv[4 * h] = v.x; xv[4 * h + 1] = v.y; xv[4 * h + 2] = v.z; xv[4 * h + 3] = v.w;
+      for (int h = 0; h < kScanE / 4; ++h) {
+        const int j = 4 * (h * kScanThreads + tid);
+        if (j < n)
+          *reinterpret_cast<float4*>(buf + (j / kScanE) * kRow + j % kScanE) =
+              *reinterpret_cast<const float4*>(c + base + j);
       }
     } else {
-      for (int q = 0; q < kScanE; ++q) {
-        const int j = q * kScanThreads + tid;
-        if (j < n) buf[(j / kScanE) * (kScanE + 1) + (j % kScanE)] = c[base + j];
+#pragma unroll 8
+      for (int k = 0; k < kScanE; ++k) {
+        const int j = k * kScanThreads + tid;
+        if (j < n) buf[(j / kScanE) * kRow + (j % kScanE)] = c[base + j];
       }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kScanE; ++k) xv[k] = buf[tid * (kScanE + 1) + k];
     }
-    bool end[kScanE];
-    int64_t p = (pos0 + j0) % L;  // position of the first element in its segment
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kScanE; ++k) {
-      end[k] = (p == L - 1);
-      p = end[k] ? 0 : p + 1;
+    for (int h = 0; h < kScanE / 4; ++h) {  // past n: not used
+      const float4 v = *reinterpret_cast<const float4*>(buf + q * kRow + 4 * h);
+      xv[4 * h] = v.x; xv[4 * h + 1] = v.y; xv[4 * h + 2] = v.z; xv[4 * h + 3] = v.w;
     }
-    // pass 1: this thread's map (identity for elements past the tile)
+    // position in its segment of the chunk's last element; both passes walk
+    // the chunk backwards, stepping the position down with it, and the element
+    // at position L - 1 ends a segment
+    const P Lp = (P)L;
+    const P plast = (P)((pos0 + j0 + kScanE - 1) % L);
+    // pass 1: this chunk's map (identity for elements past the tile)
     float A = 0.f, B = 1.f;
+    P p = plast;
 #pragma unroll
     for (int k = kScanE - 1; k >= 0; --k) {
       if (j0 + k < n) {
-        if (end[k]) {
+        if (p == Lp - 1) {
           A = xv[k];
           B = 0.f;
         } else {
@@ -103,19 +145,10 @@ __global__ void __launch_bounds__(kScanThreads) reward_scan_kernel(const float* 
           B *= gamma;
         }
       }
+      p = p == 0 ? Lp - 1 : p - 1;
     }
-    // inclusive suffix scan of the maps inside the wave: (A,B) o (A',B')
-    // = (A + B A', B B'), the left map applied after the right one
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const float An = __shfl_down(A, sh, 64);
-      const float Bn = __shfl_down(B, sh, 64);
-      if (lane + sh < 64) {
-        A = fmaf(B, An, A);
-        B *= Bn;
-      }
-    }
-    if (lane == 0) {
+    wave_scan_maps(A, B);  // lane l: the wave's chunks from its right end to its own
+    if (lane == 63) {      // the whole wave
       wa[wave] = A;
       wb[wave] = B;
     }
@@ -123,40 +156,47 @@ __global__ void __launch_bounds__(kScanThreads) reward_scan_kernel(const float* 
     // r after this wave's last element: the waves to the right applied to the
     // tile's carry, in order from the rightmost
     float X = carry_in;
-    for (int w = 3; w > wave; --w) X = fmaf(wb[w], X, wa[w]);
-    const float R = fmaf(B, X, A);  // r at this thread's first element
-    float cin = __shfl_down(R, 1, 64);
-    if (lane == 63) cin = X;
-    if (tid == 0) tile_carry = R;
+    for (int w = kScanWaves - 1; w > wave; --w) X = fmaf(wb[w], X, wa[w]);
+    const float R = fmaf(B, X, A);  // r at this chunk's first element
+    // r after this chunk: R of the chunk to its right (lane - 1), X for lane 0
+    const float cin = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(X),
+                                                                 __float_as_int(R), 0x138, 0xf,
+                                                                 0xf, false));  // wave_shr:1
+    if (q == 0) tile_carry = R;
     // pass 2: the true values
     float rho = cin;
+    p = plast;
 #pragma unroll
     for (int k = kScanE - 1; k >= 0; --k) {
       if (j0 + k < n) {  // elements past the tile's end do not exist
-        rho = end[k] ? xv[k] : fmaf(gamma, rho, xv[k]);
+        rho = p == Lp - 1 ? xv[k] : fmaf(gamma, rho, xv[k]);
         xv[k] = rho;
       }
+      p = p == 0 ? Lp - 1 : p - 1;
     }
+#pragma unroll
+    for (int h = 0; h < kScanE / 4; ++h)
+      *reinterpret_cast<float4*>(buf + q * kRow + 4 * h) =
+          make_float4(xv[4 * h], xv[4 * h + 1], xv[4 * h + 2], xv[4 * h + 3]);
+    __syncthreads();
     if constexpr (kVec) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        if (j0 + 4 * h < n)
-          *reinterpret_cast<float4*>(r + base + j0 + 4 * h) =
-              make_float4(xv[4 * h], xv[4 * h + 1], xv[4 * h + 2], xv[4 * h + 3]);
-      __syncthreads();  // wa, wb and tile_carry are read before the next tile
-      return tile_carry;
-    } else {
-#pragma unroll
-      for (int k = 0; k < kScanE; ++k) buf[tid * (kScanE + 1) + k] = xv[k];
-      __syncthreads();
-      for (int q = 0; q < kScanE; ++q) {
-        const int j = q * kScanThreads + tid;
-        if (j < n) r[base + j] = buf[(j / kScanE) * (kScanE + 1) + (j % kScanE)];
+      for (int h = 0; h < kScanE / 4; ++h) {
+        const int j = 4 * (h * kScanThreads + tid);
+        if (j < n)
+          *reinterpret_cast<float4*>(r + base + j) =
+              *reinterpret_cast<const float4*>(buf + (j / kScanE) * kRow + j % kScanE);
       }
-      const float out = tile_carry;
-      __syncthreads();  // buf and tile_carry are reused by the next tile
-      return out;
+    } else {
+#pragma unroll 8
+      for (int k = 0; k < kScanE; ++k) {
+        const int j = k * kScanThreads + tid;
+        if (j < n) r[base + j] = buf[(j / kScanE) * kRow + (j % kScanE)];
+      }
     }
+    const float out = tile_carry;
+    __syncthreads();  // buf, wa, wb and tile_carry are reused by the next tile
+    return out;
   };
 
   for (int64_t job = blockIdx.x; job < njobs; job += gridDim.x) {
@@ -201,12 +241,19 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
   const dim3 grid((uint32_t)(njobs < 65536 ? njobs : 65536));
   const bool vec = L % 4 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(r) % 16 == 0;
-  if (vec)
-    hipLaunchKernelGGL(reward_scan_kernel<true>, grid, dim3(kScanThreads), 0, s, c, nseg, L,
-                       gamma, r);
+  const bool narrow = L < ((int64_t)1 << 30);
+  if (vec && narrow)
+    hipLaunchKernelGGL((reward_scan_kernel<true, int32_t>), grid, dim3(kScanThreads), 0, s, c,
+                       nseg, L, gamma, r);
+  else if (vec)
+    hipLaunchKernelGGL((reward_scan_kernel<true, int64_t>), grid, dim3(kScanThreads), 0, s, c,
+                       nseg, L, gamma, r);
+  else if (narrow)
+    hipLaunchKernelGGL((reward_scan_kernel<false, int32_t>), grid, dim3(kScanThreads), 0, s, c,
+                       nseg, L, gamma, r);
   else
-    hipLaunchKernelGGL(reward_scan_kernel<false>, grid, dim3(kScanThreads), 0, s, c, nseg, L,
-                       gamma, r);
+    hipLaunchKernelGGL((reward_scan_kernel<false, int64_t>), grid, dim3(kScanThreads), 0, s, c,
+                       nseg, L, gamma, r);
   return hipGetLastError();
 }
 

@@ -57,7 +57,12 @@ def test_centre(K, T):
 
 @pytest.mark.parametrize("K,T,L", [(3, 60, 1), (2, 70, 7), (2, 1024, 512), (2, 1026, 513),
                                    (3, 4096, 2048), (1, 6000, 3000), (5, 600, 600),
-                                   (2, 8200, 4100), (2, 2046, 1023)])
+                                   (2, 8200, 4100), (2, 2046, 1023), (3, 9000, 9),
+                                   # one segment per tile, and segments longer than a
+                                   # tile (8192): carried from tile to tile, with a
+                                   # ragged first tile, vectorised or not
+                                   (2, 16384, 8192), (2, 20000, 10000), (2, 16388, 8194),
+                                   (1, 17001, 17001)])
 @pytest.mark.parametrize("gamma", [0.0, 0.5, 0.9, 1.0])
 def test_reward_scan(K, T, L, gamma):
     dust = need_gpu()
