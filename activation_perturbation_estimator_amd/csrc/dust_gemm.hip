@@ -82,9 +82,17 @@ struct Cfg {
   static_assert(kS * kStage <= 160 * 1024, "LDS of one CU");
 };
 
+// Workgroups per launch: one per two CUs.  On a full grid the burst of
+// matrix work at the end of each estimate (changing fp16 data through LDS on
+// every CU) pulls the shader clock of some MI355X parts down, from about 2.38
+// to 2.12-2.16 GHz, for the whole of the next call's VALU-bound head kernel
+// (10% of the step); on half the CUs the same parts keep 2.37-2.39 GHz, and
+// the G_W stage itself takes about 20 us longer.
+constexpr int64_t kGemmGridTarget = 128;
+
 // Two tile shapes, chosen per call (plan16): 256 x 256 tiles (8 waves, two per
-// SIMD, of 64 x 128) fill the chip with at most 8 token splits when the
-// output has at least 32 such tiles (N d >= 2^21); smaller outputs take
+// SIMD, of 64 x 128) reach the grid target with at most 8 token splits when
+// the output has at least 16 such tiles (N d >= 2^20); smaller outputs take
 // 256 x 128 tiles (4 waves of 64 x 128), which need half the splits and so
 // half the partial bytes.
 using WideCfg = Cfg<4, 2, 64, 128, 32, 4>;
@@ -500,8 +508,8 @@ static Gemm16Geom plan16_t(int64_t T, int64_t M, int64_t d) {
   g.tiles_m = (M + C::kBM - 1) / C::kBM;
   g.tiles_n = (d + C::kBN - 1) / C::kBN;
   const int64_t tiles = g.tiles_m * g.tiles_n;
-  // One wave of workgroups over the 256 CUs, with >= 1024 tokens per split.
-  int64_t want = (256 + tiles - 1) / tiles;
+  // kGemmGridTarget workgroups, with >= 1024 tokens per split.
+  int64_t want = (kGemmGridTarget + tiles - 1) / tiles;
   int64_t cap = (T + 1023) / 1024;
   if (cap < 1) cap = 1;
   int64_t ns = want < cap ? want : cap;
