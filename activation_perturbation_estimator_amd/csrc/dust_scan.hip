@@ -215,6 +215,136 @@ __global__ void __launch_bounds__(kScanThreads) reward_scan_kernel(const float* 
   }
 }
 
+// The same scan for segments of kWaveBlock to kScanTile elements, one wave per
+// segment and no LDS or barriers: the wave walks its segment from the end in
+// blocks of 64 x 4 elements (lane 0 holds the block's last 4 elements, lane 63
+// its first 4: every load and store of a block is one contiguous 1 KiB), in
+// groups of kWaveDepth blocks held in registers.  Per block: each lane reduces
+// its 4 elements to a map r_first = A + gamma^4 r_after, the wave's maps are
+// scanned (wave_scan_maps), and r after the block comes in as the carry of the
+// block to its right (0 at the segment's end, where r = c).  A group's loads
+// are all issued at once, and the next group's loads go out before this
+// group's stores: loads and stores may complete in any order relative to each
+// other, so a wave can only wait for all of its memory operations, and this
+// order makes one wait cover both.  Each wave depends on nothing but its own
+// data, so waves whose loads arrive early store while others still load, as in
+// a copy; the tile kernel above reads its whole tile (and waits at barriers for
+// all of its waves) before it writes any of it.
+constexpr int kWaveE = 4;
+constexpr int kWaveBlock = 64 * kWaveE;
+constexpr int kWaveDepth = 8;  // blocks per group: seq_len 2048 is one group
+constexpr int kWaveSegs = 1;   // waves (segments) per workgroup
+constexpr int kNonTemporal = 2;  // cache-policy bits of a buffer store: nt
+
+typedef unsigned int scan_u32x4_t __attribute__((ext_vector_type(4)));
+typedef float scan_f32x4_t __attribute__((ext_vector_type(4)));
+
+// kDirect (L % kWaveBlock == 0 and 16-byte accesses): every lane's elements
+// exist in every block, so loads and stores are plain and unconditional.
+// Otherwise they go through buffer resources spanning the wave's segment:
+// the elements before the segment's start, which only the first block has,
+// read as zeros and are not written, with no branch and no mask (a masked
+// store would make each store wait for the previous one).  The stores are
+// non-temporal (nothing reads r again in this kernel): at the hidden-layer
+// workload that takes a launch from 6.5 to 5.1 us.
+template <bool kDirect, bool kVec>
+__global__ void __launch_bounds__(64 * kWaveSegs) reward_scan_wave_kernel(const float* c,
+                                                                         int64_t nseg, int64_t L,
+                                                                         float gamma, float* r) {
+  const int lane = threadIdx.x & 63;
+  const int64_t seg =
+      ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kWaveSegs + (threadIdx.x >> 6);
+  if (seg >= nseg) return;  // whole wave
+  const int64_t nblk = (L + kWaveBlock - 1) / kWaveBlock;
+  const float g2 = gamma * gamma, g4 = g2 * g2;
+  const int64_t s0 = seg * L;
+  // this lane's elements of block b: [e0 - b kWaveBlock, + 4) of the segment,
+  // negative indices past its start
+  const int e0 = (int)L - kWaveE * (lane + 1);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(c + s0), 0, (int)(L * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc(r + s0, 0, (int)(L * 4), 0x00020000);
+  auto load_group = [&](int64_t b0, float(&x)[kWaveDepth][kWaveE]) {
+#pragma unroll
+    for (int u = 0; u < kWaveDepth; ++u) {
+      if (b0 + u < nblk) {
+        const int e = e0 - (int)(b0 + u) * kWaveBlock;
+        if constexpr (kDirect) {
+          const float4 q = *reinterpret_cast<const float4*>(c + s0 + e);
+          x[u][0] = q.x;
+          x[u][1] = q.y;
+          x[u][2] = q.z;
+          x[u][3] = q.w;
+        } else if constexpr (kVec) {  // L % 4 == 0: a lane's 4 elements all exist or none does
+          const scan_u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rc, 4 * e, 0, 0);
+#pragma unroll
+          for (int k = 0; k < kWaveE; ++k) x[u][k] = __uint_as_float(q[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kWaveE; ++k)
+            x[u][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rc, 4 * (e + k), 0, 0));
+        }
+      }
+    }
+  };
+  float carry = 0.f;  // r after the block: nothing after the segment's end
+  auto scan_group = [&](int64_t b0, float(&x)[kWaveDepth][kWaveE]) {
+#pragma unroll
+    for (int u = 0; u < kWaveDepth; ++u) {
+      if (b0 + u < nblk) {
+        float(&v)[kWaveE] = x[u];
+        float A = 0.f, B = g4;
+#pragma unroll
+        for (int k = kWaveE - 1; k >= 0; --k) A = fmaf(gamma, A, v[k]);
+        wave_scan_maps(A, B);  // lane l: the block's lanes 0..l, right to left
+        const float R = fmaf(B, carry, A);  // r at this lane's first element
+        // r after this lane's elements: R of lane - 1, the carry for lane 0
+        float rho = __int_as_float(__builtin_amdgcn_update_dpp(
+            __float_as_int(carry), __float_as_int(R), 0x138, 0xf, 0xf, false));  // wave_shr:1
+#pragma unroll
+        for (int k = kWaveE - 1; k >= 0; --k) {
+          rho = fmaf(gamma, rho, v[k]);
+          v[k] = rho;
+        }
+        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R), 63));
+      }
+    }
+  };
+  auto store_group = [&](int64_t b0, const float(&x)[kWaveDepth][kWaveE]) {
+#pragma unroll
+    for (int u = 0; u < kWaveDepth; ++u) {
+      if (b0 + u < nblk) {
+        const int e = e0 - (int)(b0 + u) * kWaveBlock;
+        if constexpr (kDirect) {
+          const scan_f32x4_t q = {x[u][0], x[u][1], x[u][2], x[u][3]};
+          __builtin_nontemporal_store(q, reinterpret_cast<scan_f32x4_t*>(r + s0 + e));
+        } else if constexpr (kVec) {
+          const scan_u32x4_t q = {__float_as_uint(x[u][0]), __float_as_uint(x[u][1]),
+                                  __float_as_uint(x[u][2]), __float_as_uint(x[u][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(q, rr, 4 * e, 0, kNonTemporal);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kWaveE; ++k)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[u][k]), rr, 4 * (e + k), 0,
+                                                 kNonTemporal);
+        }
+      }
+    }
+  };
+  float x[kWaveDepth][kWaveE], y[kWaveDepth][kWaveE];
+  load_group(0, x);
+  for (int64_t b0 = 0; b0 < nblk; b0 += 2 * kWaveDepth) {
+    scan_group(b0, x);
+    if (b0 + kWaveDepth < nblk) load_group(b0 + kWaveDepth, y);
+    store_group(b0, x);
+    if (b0 + kWaveDepth >= nblk) break;
+    scan_group(b0 + kWaveDepth, y);
+    if (b0 + 2 * kWaveDepth < nblk) load_group(b0 + 2 * kWaveDepth, x);
+    store_group(b0 + kWaveDepth, y);
+  }
+}
+
 __global__ void zero_flag_kernel(int32_t* flag) { *flag = 0; }
 
 __global__ void __launch_bounds__(256) check_targets_kernel(const int32_t* __restrict__ y,
@@ -236,11 +366,29 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
                               float* r, hipStream_t s) {
   const int64_t nseg = K * (T / L);
   if (nseg == 0) return hipSuccess;
+  const bool vec = L % 4 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(r) % 16 == 0;
+  if (L >= kWaveBlock && L <= kScanTile) {  // one wave per segment
+    // groups <= 2^32 (K T <= 2^40); grid x times the block stays below 2^32,
+    // and the grid holds fewer than gy groups more than there are
+    const int64_t groups = (nseg + kWaveSegs - 1) / kWaveSegs;
+    const int64_t gy = (groups + ((int64_t)1 << 24) - 1) >> 24;
+    const dim3 grid((uint32_t)((groups + gy - 1) / gy), (uint32_t)gy);
+    const dim3 block(64 * kWaveSegs);
+    if (vec && L % kWaveBlock == 0)
+      hipLaunchKernelGGL((reward_scan_wave_kernel<true, true>), grid, block, 0, s, c, nseg, L,
+                         gamma, r);
+    else if (vec)
+      hipLaunchKernelGGL((reward_scan_wave_kernel<false, true>), grid, block, 0, s, c, nseg, L,
+                         gamma, r);
+    else
+      hipLaunchKernelGGL((reward_scan_wave_kernel<false, false>), grid, block, 0, s, c, nseg, L,
+                         gamma, r);
+    return hipGetLastError();
+  }
   const int64_t m = L > kScanTile ? 1 : kScanTile / L;
   const int64_t njobs = (nseg + m - 1) / m;
   const dim3 grid((uint32_t)(njobs < 65536 ? njobs : 65536));
-  const bool vec = L % 4 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(r) % 16 == 0;
   const bool narrow = L < ((int64_t)1 << 30);
   if (vec && narrow)
     hipLaunchKernelGGL((reward_scan_kernel<true, int32_t>), grid, dim3(kScanThreads), 0, s, c,

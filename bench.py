@@ -325,17 +325,21 @@ def run_linear(args, torch, dust, synth, w):
     acc_bytes = 4.0 * w.K * w.T + 4.0 * w.T * w.V
     out["roofline"]["hbm_gbs"] = acc_bytes / (ee_ms / 1e3) / 1e9
     out["roofline"]["hbm_frac"] = acc_bytes / (ee_ms / 1e3) / HBM_BYTES_PER_S
-    # the scan is ~10 us, so the stage events around it carry the launch gaps:
-    # its per-launch time comes from back-to-back calls between two events
+    # the scan takes a few microseconds, less than a call from Python takes to
+    # launch it, so the stage events around it (and back-to-back calls) time the
+    # host: its per-launch time comes from a HIP graph of SCAN_LAUNCHES scans,
+    # replayed between two events
     rbuf = torch.empty((w.K, w.T), dtype=torch.float32, device=dev)
-    scan_ms = _time_calls(torch, lambda: dust.reward_scan(cd, seq_len=w.seq_len, gamma=w.gamma,
-                                                          out=rbuf), SCAN_LAUNCHES, 2)
+    scan = lambda: dust.reward_scan(cd, seq_len=w.seq_len, gamma=w.gamma, out=rbuf)
+    scan_ms = _time_graph(torch, scan, SCAN_LAUNCHES)
+    scan_eager_ms = _time_calls(torch, scan, SCAN_LAUNCHES, 2)
     del rbuf
     out["reward_scan"] = {"bound": "hbm", "achieved": scan_bytes / (scan_ms / 1e3) / 1e9,
                           "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
                           "frac": scan_bytes / (scan_ms / 1e3) / HBM_BYTES_PER_S,
                           "launch_ms": scan_ms, "launches": SCAN_LAUNCHES,
-                          "stage_ms": stage[0]}
+                          "timing": "one HIP graph of back-to-back launches",
+                          "eager_launch_ms": scan_eager_ms, "stage_ms": stage[0]}
     out["stages_ms"] = {"reward_scan": stage[0], "error_estimate": stage[1], "outer_sum": stage[2]}
     out["outer_sum"] = outer_sum_fields(w, stage[2])
     if not args.no_cpu_baseline:
@@ -357,6 +361,28 @@ def _time_calls(torch, fn, steps: int, warmup: int) -> float:
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def _time_graph(torch, fn, calls: int) -> float:
+    """ms per call of fn, from one HIP graph of `calls` back-to-back calls
+    (captured on a side stream, replayed once untimed, then timed between two
+    events on the stream that replays it)."""
+    fn()  # the library loads and the kernels' code objects settle before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / calls
 
 
 def _row_line(args, metric, value, unit, ms, workload, roofline, extra=None):

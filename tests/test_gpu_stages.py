@@ -176,6 +176,59 @@ def test_check_targets():
     assert not dust.check_targets(y, 100)
 
 
+@pytest.mark.parametrize("L,gamma", [(1024, 0.9), (1000, 0.9), (256, 1.0), (260, 0.5),
+                                     (2048, 0.0)])
+def test_reward_scan_unaligned(L, gamma):
+    """c and r 4 bytes past a 16-byte boundary: the one-wave-per-segment scan
+    then reads and writes element by element, through buffer resources bounded
+    by the segment.  Nothing outside r is written."""
+    dust = need_gpu()
+    import torch
+    K, T = 3, 4 * L
+    c = np.random.default_rng(L).standard_normal((K, T)).astype(np.float32)
+    cb = torch.zeros(K * T + 1, dtype=torch.float32, device="cuda")
+    cb[1:] = torch.from_numpy(c.reshape(-1)).cuda()
+    rb = torch.full((K * T + 2,), float("nan"), dtype=torch.float32, device="cuda")
+    cv, rv = cb[1:].view(K, T), rb[1:K * T + 1].view(K, T)
+    assert cv.data_ptr() % 16 == 4 and rv.data_ptr() % 16 == 4
+    dust.reward_scan(cv, seq_len=L, gamma=gamma, out=rv)
+    torch.cuda.synchronize()
+    got = rb.cpu().numpy()
+    assert np.isnan(got[0]) and np.isnan(got[-1])
+    ref = oracle.reward_scan(c.astype(np.float64), L, gamma)
+    if gamma == 0.0:
+        assert np.array_equal(got[1:-1].reshape(K, T), c)
+    else:
+        assert rel_l2(got[1:-1].reshape(K, T), ref) <= 1e-5
+
+
+def test_reward_scan_two_dimensional_grid():
+    """2^24 + 1024 segments of 256 tokens (16 GiB per array): more one-wave
+    workgroups than the launch puts in the grid's x dimension (2^24), so it
+    adds a second one.  The input comes from torch's seeded generator on the
+    device; segments sampled across the array, around the end of the first
+    grid row and at the end, against the oracle."""
+    dust = need_gpu()
+    import torch
+    L, gamma = 256, 0.9
+    nseg = (1 << 24) + 1024
+    T = nseg * L
+    gen = torch.Generator(device="cuda").manual_seed(24)
+    c = torch.randn((1, T), generator=gen, dtype=torch.float32, device="cuda")
+    r = dust.reward_scan(c, seq_len=L, gamma=gamma)
+    torch.cuda.synchronize()
+    segs = np.concatenate([np.arange(4), np.arange((1 << 24) - 4, (1 << 24) + 8),
+                           np.arange(nseg - 4, nseg),
+                           np.random.default_rng(1).choice(nseg, 200, replace=False)])
+    for sgi in segs:
+        lo = int(sgi) * L
+        cs = c[0, lo:lo + L].cpu().numpy().astype(np.float64).reshape(1, L)
+        ref = oracle.reward_scan(cs, L, gamma)
+        assert rel_l2(r[0, lo:lo + L].cpu().numpy().reshape(1, L), ref) <= 1e-5, sgi
+    del c, r
+    torch.cuda.empty_cache()
+
+
 def test_reward_scan_many_short_segments():
     """K * T / L = 524288 (draw, sequence) segments of 2 tokens: a tile of the
     scan holds 1024 whole segments, so nearly every thread's elements span a
