@@ -191,6 +191,110 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   info[pos] = (uint32_t)v | ((lo / kSeg == (hi - 1) / kSeg) ? 0x80000000u : 0u);
 }
 
+// Steps 1-4 in one launch, for T <= kOneT tokens and vocabularies of up to
+// kOneVocab ids: one workgroup per chunk of kChunk tokens, each of which also
+// counts every id in LDS over all T tokens and over the tokens before its
+// chunk (integer atomics: the counts do not depend on their order) -- the ids
+// are only 4T bytes, so every workgroup reading all of them costs less than
+// the three launches that would otherwise share the counts.  The totals'
+// exclusive scan gives the ids' starts.  Within the chunk, each wave ranks its
+// 64 tokens among equal ids by ballots over the id's bits (a lane's peers are
+// the AND over bits b of ballot(bit b set) or its complement), and its count of
+// each id goes to an LDS row of the wave; a token's position is then
+//   start[id] + (the id's tokens in earlier chunks) + (in earlier waves of the
+//   chunk) + (its peers in lower lanes):
+// ascending id, and ascending token within an id.
+constexpr int64_t kOneT = 32768;
+constexpr int64_t kOneVocab = 4096;
+constexpr int kOneWaves = kChunk / 64;
+
+__global__ void __launch_bounds__(kChunk) one_pass_sort_kernel(const int32_t* __restrict__ ids,
+                                                               int64_t T, int64_t vocab,
+                                                               int32_t* __restrict__ order,
+                                                               uint32_t* __restrict__ info,
+                                                               int32_t* __restrict__ start) {
+  __shared__ __attribute__((aligned(16))) uint16_t wcnt[kOneWaves * kOneVocab];
+  __shared__ int32_t hall[kOneVocab + 1], hbefore[kOneVocab];
+  __shared__ int32_t wsum[kOneWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = (int)vocab, Ti = (int)T;
+  const int c0 = (int)blockIdx.x * kChunk;  // this chunk's first token
+  const int t = c0 + tid;
+  const int mine = t < Ti ? ids[t] : -1;
+  for (int i = tid; i < kOneWaves * kOneVocab / 8; i += kChunk)
+    reinterpret_cast<uint4*>(wcnt)[i] = make_uint4(0, 0, 0, 0);
+  for (int v = tid; v < V; v += kChunk) {
+    hall[v] = 0;
+    hbefore[v] = 0;
+  }
+  __syncthreads();
+  // counts of every id, over all tokens and over those before the chunk
+  constexpr int kU = 16;
+  for (int b = 0; b < Ti; b += kChunk * kU) {
+    int v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tt = b + u * kChunk + tid;
+      v[u] = tt < Ti ? ids[tt] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (v[u] >= 0 && v[u] < V) {
+        atomicAdd(&hall[v[u]], 1);
+        if (b + u * kChunk + tid < c0) atomicAdd(&hbefore[v[u]], 1);
+      }
+  }
+  __syncthreads();
+  // exclusive scan of the totals: kChunk threads, 8 consecutive ids each
+  constexpr int kPer = kOneVocab / kChunk;
+  {
+    int x[kPer], sum = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int v = kPer * tid + e;
+      x[e] = v < V ? hall[v] : 0;
+      sum += x[e];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int ww = 0; ww < w; ++ww) run += wsum[ww];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int v = kPer * tid + e;
+      if (v < V) hall[v] = run;
+      run += x[e];
+    }
+    if (tid == kChunk - 1) hall[V] = run;  // the number of valid tokens
+  }
+  // this wave's peers of each token, and the wave's count of each id
+  const bool valid = mine >= 0 && mine < V;
+  const int nbits = V > 1 ? 32 - __clz(V - 1) : 0;
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((mine >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  if (valid && (m >> lane) == 1ull) wcnt[w * kOneVocab + mine] = (uint16_t)__popcll(m);
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int v = tid; v <= V; v += kChunk) start[v] = hall[v];
+  if (valid) {
+    int pos = hall[mine] + hbefore[mine] + __popcll(m & ((1ull << lane) - 1));
+    for (int ww = 0; ww < w; ++ww) pos += wcnt[ww * kOneVocab + mine];
+    const int lo = hall[mine], hi = hall[mine + 1];
+    order[pos] = t;
+    info[pos] = (uint32_t)mine | ((lo / kSeg == (hi - 1) / kSeg) ? 0x80000000u : 0u);
+  }
+}
+
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
@@ -329,24 +433,30 @@ hipError_t launch_embedding_grad(const int32_t* ids, const float* g, int64_t T, 
   w += a256((size_t)(vocab + 1) * 4);
   float* part = reinterpret_cast<float*>(w);
 
-  // small vocabularies: each rank workgroup writes its whole row of counts
-  const int full_row = vocab <= kRankRowMax;
-  if (!full_row) {
-    const int64_t ncnt = C * vocab;
-    int64_t zb = (ncnt + 255) / 256;
-    if (zb > 4096) zb = 4096;
-    hipLaunchKernelGGL(zero_i32_kernel, dim3((uint32_t)(zb > 0 ? zb : 1)), dim3(256), 0, s, counts,
-                       ncnt);
+  if (T <= kOneT && vocab <= kOneVocab) {  // steps 1-4 in one launch
+    hipLaunchKernelGGL(one_pass_sort_kernel, dim3((uint32_t)(C > 0 ? C : 1)), dim3(kChunk), 0, s,
+                       ids, T, vocab, order, info, start);
+  } else {
+    // small vocabularies: each rank workgroup writes its whole row of counts
+    const int full_row = vocab <= kRankRowMax;
+    if (!full_row) {
+      const int64_t ncnt = C * vocab;
+      int64_t zb = (ncnt + 255) / 256;
+      if (zb > 4096) zb = 4096;
+      hipLaunchKernelGGL(zero_i32_kernel, dim3((uint32_t)(zb > 0 ? zb : 1)), dim3(256), 0, s,
+                         counts, ncnt);
+    }
+    if (T > 0)
+      hipLaunchKernelGGL(rank_kernel, dim3((uint32_t)C), dim3(kChunk), 0, s, ids, T, vocab, rank,
+                         counts, full_row);
+    hipLaunchKernelGGL(row_offsets_kernel, dim3((uint32_t)((vocab + 255) / 256)), dim3(256), 0, s,
+                       counts, C, vocab, total);
+    hipLaunchKernelGGL(id_scan_kernel, dim3(1), dim3(1024), 0, s, total, vocab, start);
+    if (T > 0)
+      hipLaunchKernelGGL(scatter_kernel, dim3((uint32_t)((T + 255) / 256)), dim3(256), 0, s, ids,
+                         T, vocab, rank, counts, start, order, info);
   }
-  if (T > 0)
-    hipLaunchKernelGGL(rank_kernel, dim3((uint32_t)C), dim3(kChunk), 0, s, ids, T, vocab, rank,
-                       counts, full_row);
-  hipLaunchKernelGGL(row_offsets_kernel, dim3((uint32_t)((vocab + 255) / 256)), dim3(256), 0, s,
-                     counts, C, vocab, total);
-  hipLaunchKernelGGL(id_scan_kernel, dim3(1), dim3(1024), 0, s, total, vocab, start);
   if (T > 0) {
-    hipLaunchKernelGGL(scatter_kernel, dim3((uint32_t)((T + 255) / 256)), dim3(256), 0, s, ids, T,
-                       vocab, rank, counts, start, order, info);
     hipLaunchKernelGGL(segment_kernel, dim3((uint32_t)S, (uint32_t)CB), dim3(kSegCols), 0, s, g, N,
                        T, start, vocab, order, info, GE, part);
   }

@@ -19,7 +19,11 @@ pytestmark = pytest.mark.gpu
                                               (300, 4, 5, "invalid"),
                                               # vocabulary above the in-pass clear of the
                                               # counts; more chunks than one batch of 32
-                                              (3000, 8, 20000, "zipf"), (20000, 16, 300, "zipf")])
+                                              (3000, 8, 20000, "zipf"), (20000, 16, 300, "zipf"),
+                                              # the largest one-launch sort, and one token or
+                                              # one id past it
+                                              (32768, 8, 4096, "zipf"), (32769, 8, 4096, "zipf"),
+                                              (16384, 8, 4097, "zipf")])
 def test_embedding_grad(T, N, vocab, layout):
     """Zipf ids (a few ids own long runs that span many 32-position segments of
     the sorted order), ids whose runs fill segments exactly or straddle them,
