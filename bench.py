@@ -435,7 +435,7 @@ def run_embedding(args, torch, dust, synth):
                      args.steps, args.warmup)
     nbytes = 4.0 * T * N + 4.0 * vocab * N + 4.0 * T
     gbs = nbytes / (ms / 1e3) / 1e9
-    roof = {"bound": "hbm", "kernel": "rank/scan/scatter/gather (dust_embedding_grad)",
+    roof = {"bound": "hbm", "kernel": "sort/segment/finish (dust_embedding_grad)",
             "achieved": gbs, "peak": HBM_BYTES_PER_S / 1e9, "unit": "GB/s",
             "frac": gbs * 1e9 / HBM_BYTES_PER_S, "traffic": None, "launch_ms": ms}
     return _row_line(args, f"tokens/sec, embedding estimate G_E (T={T}, N={N}, vocab={vocab})",
