@@ -9,7 +9,7 @@ fused noise + cross-entropy + accumulate kernel, timed with HIP events on the
 call's stream inside the timed loop) and the fp64 CPU oracle's rate on a
 bounded sample of the same workload.
 
-  python bench.py [--steps 10] [--warmup 2] [--workload paper] [--no-cpu-baseline]
+  python bench.py [--steps 20] [--warmup 5] [--workload paper] [--no-cpu-baseline]
                   [--copy-probe-mib 256]
 
 The default line also carries sub-records ("workloads") for the K = 16384 LM
@@ -107,8 +107,8 @@ def measured_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="paper",
                     help="paper (default: T=16384, V=4096, d=512, K=64), k1024, k16384, tiny, "
                          "linear (hidden layer 512->2048, K=256, gamma=0.9); the other rows: "
