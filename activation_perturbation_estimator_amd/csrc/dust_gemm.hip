@@ -454,9 +454,10 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
     const int64_t e = 4 * e4;
     float v[4];
     if (e + 4 <= n) {
-      // split order; four partials loaded at a time so that their reads overlap
-      float4 s = reinterpret_cast<const float4*>(part)[e4];
-      int64_t q = 1;
+      // split order (0 + p0 = p0 exactly); four partials loaded at a time so
+      // that their reads overlap: the usual 4 or 8 splits take 1 or 2 round trips
+      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+      int64_t q = 0;
       for (; q + 4 <= nsplit; q += 4) {
         float4 w[4];
 #pragma unroll
