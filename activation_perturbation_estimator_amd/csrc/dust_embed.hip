@@ -228,7 +228,10 @@ __global__ void __launch_bounds__(kChunk) one_pass_sort_kernel(const int32_t* __
     hbefore[v] = 0;
   }
   __syncthreads();
-  // counts of every id, over all tokens and over those before the chunk
+  // counts of every id, over all tokens and over those before the chunk; the
+  // chunks in the second half count the tokens from the chunk on instead (fewer)
+  // and subtract
+  const bool before = 2 * c0 <= Ti;
   constexpr int kU = 16;
   for (int b = 0; b < Ti; b += kChunk * kU) {
     int v[kU];
@@ -241,10 +244,12 @@ __global__ void __launch_bounds__(kChunk) one_pass_sort_kernel(const int32_t* __
     for (int u = 0; u < kU; ++u)
       if (v[u] >= 0 && v[u] < V) {
         atomicAdd(&hall[v[u]], 1);
-        if (b + u * kChunk + tid < c0) atomicAdd(&hbefore[v[u]], 1);
+        if ((b + u * kChunk + tid < c0) == before) atomicAdd(&hbefore[v[u]], 1);
       }
   }
   __syncthreads();
+  if (!before)  // hbefore holds the counts from the chunk on: subtract them
+    for (int v = tid; v < V; v += kChunk) hbefore[v] = hall[v] - hbefore[v];
   // exclusive scan of the totals: kChunk threads, 8 consecutive ids each
   constexpr int kPer = kOneVocab / kChunk;
   {
