@@ -249,7 +249,8 @@ dust_status dust_perturbed_linear(const void* X, const void* W, dust_dtype dt, i
 /* Embedding layer (paper digest, section 2.2: a one-hot input turns the outer
  * product into a scatter-add): G_E[v,:] = sum over tokens t with ids[t] = v of
  * g_hat[t,:], the rows taken in increasing t (in blocks of 32 of the id-sorted
- * order; deterministic, no atomics; rows of unused ids are 0; ids outside
+ * order; deterministic: no float atomics, and the sort's integer counts do not
+ * depend on the order of their adds; rows of unused ids are 0; ids outside
  * [0, vocab) are skipped).
  *   ids device [T] int32; g_hat device [T,N] fp32 (N % 4 == 0);
  *   G_E device [vocab,N] fp32 out;
