@@ -89,8 +89,9 @@ def _events(stage_events) -> Optional[object]:
     if len(stage_events) != DUST_STAGE_EVENTS:
         raise ValueError(f"stage_events needs {DUST_STAGE_EVENTS} events")
     arr = (ctypes.c_void_p * DUST_STAGE_EVENTS)()
-    for k, ev in enumerate(stage_events):
-        arr[k] = int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev)
+    for k, ev in enumerate(stage_events):  # None: that stage boundary is not recorded
+        if ev is not None:
+            arr[k] = int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev)
     return arr
 
 
@@ -143,7 +144,9 @@ def head_estimate(logits, targets, X, *, sigma: float, K: int, gamma: float = 0.
 
     logits [T,V] (f32/bf16), targets [T] int32, X [T,d] (f32/bf16), all on one
     GPU.  Returns (g_hat [T,V] f32, G_W [V,d] f32) and, with return_losses,
-    the per-draw losses [K,T].  ``out`` may pass preallocated (g_hat, G_W)."""
+    the per-draw losses [K,T].  ``out`` may pass preallocated (g_hat, G_W).
+    ``stage_events``: DUST_STAGE_EVENTS torch.cuda.Event objects (or None for a
+    boundary that is not to be recorded) marking the stages on the stream."""
     torch = _torch()
     T, V = logits.shape
     d = X.shape[1]

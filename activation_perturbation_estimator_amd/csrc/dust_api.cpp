@@ -69,7 +69,7 @@ dust_status hip_status(hipError_t e) { return e == hipSuccess ? DUST_OK : DUST_E
 hipStream_t as_stream(dust_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 hipError_t record(const dust_event_t* ev, int k, hipStream_t s) {
-  if (ev == nullptr) return hipSuccess;
+  if (ev == nullptr || ev[k] == nullptr) return hipSuccess;  // a NULL entry is not recorded
   return hipEventRecord(reinterpret_cast<hipEvent_t>(ev[k]), s);
 }
 

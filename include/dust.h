@@ -132,7 +132,10 @@ const char* dust_version(void);
  *   stage_events  NULL, or DUST_STAGE_EVENTS events recorded on s: [0] before
  *           the first kernel, [1] after the per-draw loss / fused estimate
  *           stage, [2] after the error-estimate stage, [3] after the outer
- *           product.  Stages a call skips record back to back.
+ *           product.  Stages a call skips record back to back.  A NULL entry
+ *           is not recorded (each record puts a few microseconds of marker
+ *           between the kernels, so a timing loop can drop the ones it does
+ *           not need, e.g. [0] when the previous call's [3] marks the start).
  * Requires V % 4 == 0, V <= DUST_N_MAX, T % seq_len == 0. */
 dust_status dust_head_estimate(const void* logits, dust_dtype logits_dt,
                                const int32_t* targets,

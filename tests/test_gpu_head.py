@@ -162,3 +162,26 @@ def test_largest_sigma(gamma):
     # kernels accept (|sigma a| up to 8 x 5.77 nats above the clean maximum)
     z, y, X = synth.head_inputs(64, 1000, 24, seed=22, bf16=False)
     _check(z, y, X, sigma=8.0, K=16, gamma=gamma, seed=2, seq_len=16)
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.9])
+def test_stage_events(gamma):
+    """Stage events, all four or with entries left NULL (not recorded), change
+    nothing in the results; every recorded boundary is ordered after the one
+    before it on the call's stream."""
+    dust = need_gpu()
+    import torch
+    z, y, X = synth.head_inputs(256, 1024, 32, seed=12, bf16=True)
+    ref = _run(dust, z, y, X, sigma=0.05, K=9, gamma=gamma, seed=2, seq_len=128)
+    for mask in ((1, 1, 1, 1), (1, 1, 0, 1), (0, 1, 0, 1), (0, 0, 0, 0)):
+        evs = [torch.cuda.Event(enable_timing=True) if m else None for m in mask]
+        for e in evs:  # torch times only events it has seen recorded once
+            if e is not None:
+                e.record()
+        got = _run(dust, z, y, X, sigma=0.05, K=9, gamma=gamma, seed=2, seq_len=128,
+                   stage_events=evs)
+        for u, v in zip(ref, got):
+            assert np.array_equal(u, v)
+        rec = [e for e in evs if e is not None]
+        for a, b in zip(rec, rec[1:]):
+            assert a.elapsed_time(b) >= 0.0
