@@ -108,20 +108,29 @@ __device__ __forceinline__ float unit_open(uint32_t x) {
   return __uint_as_float(bits) - 0.999999940395355224609375f;
 }
 
-// Four standard normals from one Philox block, Box-Muller on (u0,u1) and
-// (u2,u3): radius sqrt(-2 ln u_even), angle 2 pi u_odd, cosine first.
-// v_log_f32 is log2, v_sin_f32 / v_cos_f32 take the angle in revolutions.
+// The Box-Muller angle of a word, in revolutions: v = (x >> 9) 2^-23 in [0, 1).
+// Returned as 1 + v, the same single instruction as unit_open without its
+// subtraction: v_sin_f32 and v_cos_f32 take their argument in revolutions and
+// reduce it modulo one, and 1 + v (exact in fp32) is the same point of the
+// circle as v.
+__device__ __forceinline__ float angle_rev_plus1(uint32_t x) {
+  return __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, x, 9u));  // (x >> 9) | 0x3F800000
+}
+
+// Four standard normals from one Philox block, Box-Muller on the word pairs
+// (0,1) and (2,3): radius sqrt(-2 ln u) from the even word's uniform, angle
+// 2 pi v from the odd word's fraction, cosine first.  v_log_f32 is log2.
 __device__ __forceinline__ void box_muller4(const u32x4& x, float& a0, float& a1, float& a2,
                                             float& a3) {
   constexpr float kMinus2Ln2 = -1.38629436111989061883f;
-  const float u0 = unit_open(x.x), u1 = unit_open(x.y);
-  const float u2 = unit_open(x.z), u3 = unit_open(x.w);
+  const float u0 = unit_open(x.x), v1 = angle_rev_plus1(x.y);
+  const float u2 = unit_open(x.z), v3 = angle_rev_plus1(x.w);
   const float r0 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(u0));
   const float r1 = __builtin_amdgcn_sqrtf(kMinus2Ln2 * __builtin_amdgcn_logf(u2));
-  a0 = r0 * __builtin_amdgcn_cosf(u1);
-  a1 = r0 * __builtin_amdgcn_sinf(u1);
-  a2 = r1 * __builtin_amdgcn_cosf(u3);
-  a3 = r1 * __builtin_amdgcn_sinf(u3);
+  a0 = r0 * __builtin_amdgcn_cosf(v1);
+  a1 = r0 * __builtin_amdgcn_sinf(v1);
+  a2 = r1 * __builtin_amdgcn_cosf(v3);
+  a3 = r1 * __builtin_amdgcn_sinf(v3);
 }
 
 // The four normals of columns 4j .. 4j+3 of a^(draw)_token.
@@ -144,14 +153,14 @@ __device__ __forceinline__ void normal4_scaled(uint32_t j, uint32_t token, uint3
                                                uint32_t stream, uint32_t k0, uint32_t k1,
                                                float& a0, float& a1, float& a2, float& a3) {
   const u32x4 x = philox10_row<kColumnOnly>(token, j, draw, stream, k0, k1);
-  const float u0 = unit_open(x.x), u1 = unit_open(x.y);
-  const float u2 = unit_open(x.z), u3 = unit_open(x.w);
+  const float u0 = unit_open(x.x), v1 = angle_rev_plus1(x.y);
+  const float u2 = unit_open(x.z), v3 = angle_rev_plus1(x.w);
   const float r0 = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u0));
   const float r1 = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u2));
-  a0 = r0 * __builtin_amdgcn_cosf(u1);
-  a1 = r0 * __builtin_amdgcn_sinf(u1);
-  a2 = r1 * __builtin_amdgcn_cosf(u3);
-  a3 = r1 * __builtin_amdgcn_sinf(u3);
+  a0 = r0 * __builtin_amdgcn_cosf(v1);
+  a1 = r0 * __builtin_amdgcn_sinf(v1);
+  a2 = r1 * __builtin_amdgcn_cosf(v3);
+  a3 = r1 * __builtin_amdgcn_sinf(v3);
 }
 
 // ---------------------------------------------------------------------------

@@ -63,10 +63,12 @@ SLOTS_PER_NORMAL_ERROR_ESTIMATE = SLOTS["philox"] + SLOTS["uniform"] + SLOTS["bo
 # The fused head kernel's own count is lower: with the column's Philox word in
 # a xor, the first rounds are the same for all lanes of a wave and 4 of the 20
 # products per block run on the scalar unit (16 x 2 + 18 xors = 12.5 per
-# normal), and the normals come scaled by 1/sqrt(2 ln 2), one multiply fewer
-# per pair (Box-Muller 9): 32.5 slots issued per normal by design.
-IMPL_SLOTS_PER_NORMAL = 32.5
-IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE = 25.5
+# normal), the normals come scaled by 1/sqrt(2 ln 2), one multiply fewer per
+# pair (Box-Muller 9), and the angle word reaches v_sin/v_cos as 1 + v (they
+# reduce modulo one revolution) without the subtraction (uniform 2.5): 32 slots
+# issued per normal by design.
+IMPL_SLOTS_PER_NORMAL = 32.0
+IMPL_SLOTS_PER_NORMAL_ERROR_ESTIMATE = 25.0
 
 # Hardware byte counts of the head kernel (FETCH_SIZE and WRITE_SIZE from two
 # rocprofv3 --pmc runs, scaled by the same counters read on a plain copy of

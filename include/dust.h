@@ -59,11 +59,13 @@
  * independent per token; this is this library's counter-based stream, which
  * dust_noise reproduces):  a^(i)_t[n] for draw i, token t, column n comes from the
  * Philox4x32-10 block (Salmon et al., SC'11) with key (seed mod 2^32,
- * seed >> 32) and counter words (t, n / 4, i, stream).  Each 32-bit output word
- * x becomes u = ((x >> 9) + 1/2) * 2^-23, and Box-Muller maps (u0,u1) to
- * columns 4j, 4j+1 (radius sqrt(-2 ln u0), angle 2 pi u1, cosine first) and
- * (u2,u3) to columns 4j+2, 4j+3.  Draw indices and token indices are 0-based
- * within the call.
+ * seed >> 32) and counter words (t, n / 4, i, stream), output words x0..x3.
+ * With m(x) = x >> 9 (the top 23 bits), the even words give the radius from
+ * u = (m + 1/2) * 2^-23 in (0,1) and the odd words the angle from
+ * v = m * 2^-23 in [0,1) revolutions: Box-Muller maps (x0,x1) to columns 4j,
+ * 4j+1 (radius sqrt(-2 ln u0), angle 2 pi v1, cosine first) and (x2,x3) to
+ * columns 4j+2, 4j+3.  Draw indices and token indices are 0-based within the
+ * call.
  */
 #ifndef DUST_H
 #define DUST_H

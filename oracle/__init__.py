@@ -65,6 +65,8 @@ def _load():
     lib.oracle_philox_batch.restype = None
     lib.oracle_uniform_batch.argtypes = [_u32p, _f64p, _i64]
     lib.oracle_uniform_batch.restype = None
+    lib.oracle_angle_batch.argtypes = [_u32p, _f64p, _i64]
+    lib.oracle_angle_batch.restype = None
     lib.oracle_noise.argtypes = [_u64, _u32, _i64, _i64, _i64, _i64, _f64p]
     lib.oracle_noise.restype = None
     lib.oracle_reward_scan.argtypes = [_f64p, _i64, _i64, _i64, _f64, _f64p]
@@ -135,6 +137,14 @@ def uniform(x) -> np.ndarray:
     u = np.empty(x.shape[0], dtype=np.float64)
     _load().oracle_uniform_batch(x, u, x.shape[0])
     return u
+
+
+def angle(x) -> np.ndarray:
+    """v = (x >> 9) / 2^23 for uint32 words x: the Box-Muller angle in revolutions."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.uint32)).ravel()
+    v = np.empty(x.shape[0], dtype=np.float64)
+    _load().oracle_angle_batch(x, v, x.shape[0])
+    return v
 
 
 def noise(seed: int, stream: int, draw0: int, ndraw: int, T: int, N: int) -> np.ndarray:

@@ -23,8 +23,9 @@
  * Readings taken where the pages are silent:
  *   - "centred" = subtract the per-token mean over the K draws.
  *   - noise stream = Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit
- *     seed, counter (token, column/4, draw, stream), mapped to uniforms in
- *     (0,1) by the top 23 bits, then Box-Muller (1958).
+ *     seed, counter (token, column/4, draw, stream), then Box-Muller (1958):
+ *     the radius from a uniform in (0,1) and the angle from a fraction of a
+ *     revolution in [0,1), both made from the top 23 bits of a word.
  *   - the gamma scan restarts at every sequence boundary (seq_len tokens).
  *   - G_W sums over tokens (no mean); no bias term.
  *
@@ -83,8 +84,18 @@ double oracle_uniform(uint32_t x)
     return m * 0x1p-23 + 0x1p-24;
 }
 
-/* Four standard normals of one Philox block: Box-Muller on the pairs
- * (u0,u1) and (u2,u3); radius from the even word, angle from the odd one. */
+/* Angle of Box-Muller as a fraction of a revolution, in [0,1): the top 23
+ * bits of a Philox word as an integer m, v = m / 2^23.  Exact in fp32 and
+ * fp64.  (The angle needs no offset: 0 is a valid angle, and v and v + 1 give
+ * the same point of the circle.) */
+double oracle_angle(uint32_t x)
+{
+    return (double)(x >> 9) * 0x1p-23;
+}
+
+/* Four standard normals of one Philox block: Box-Muller on the pairs of words
+ * (0,1) and (2,3); radius sqrt(-2 ln u) from the even word's uniform u, angle
+ * 2 pi v from the odd word's fraction v. */
 void oracle_normal4(uint64_t seed, uint32_t j, uint32_t t, uint32_t i, uint32_t stream,
                     double a[4])
 {
@@ -92,14 +103,14 @@ void oracle_normal4(uint64_t seed, uint32_t j, uint32_t t, uint32_t i, uint32_t 
     uint32_t ctr[4] = { t, j, i, stream };
     uint32_t x[4];
     oracle_philox4x32_10(seed, ctr, x);
-    double u0 = oracle_uniform(x[0]), u1 = oracle_uniform(x[1]);
-    double u2 = oracle_uniform(x[2]), u3 = oracle_uniform(x[3]);
+    double u0 = oracle_uniform(x[0]), v1 = oracle_angle(x[1]);
+    double u2 = oracle_uniform(x[2]), v3 = oracle_angle(x[3]);
     double rho0 = sqrt(-2.0 * log(u0));
     double rho1 = sqrt(-2.0 * log(u2));
-    a[0] = rho0 * cos(two_pi * u1);
-    a[1] = rho0 * sin(two_pi * u1);
-    a[2] = rho1 * cos(two_pi * u3);
-    a[3] = rho1 * sin(two_pi * u3);
+    a[0] = rho0 * cos(two_pi * v1);
+    a[1] = rho0 * sin(two_pi * v1);
+    a[2] = rho1 * cos(two_pi * v3);
+    a[3] = rho1 * sin(two_pi * v3);
 }
 
 /* Batch forms for the tests: n independent blocks / uniforms. */
@@ -111,6 +122,11 @@ void oracle_philox_batch(uint64_t seed, const uint32_t* ctr, uint32_t* out, int6
 void oracle_uniform_batch(const uint32_t* x, double* u, int64_t n)
 {
     for (int64_t b = 0; b < n; ++b) u[b] = oracle_uniform(x[b]);
+}
+
+void oracle_angle_batch(const uint32_t* x, double* v, int64_t n)
+{
+    for (int64_t b = 0; b < n; ++b) v[b] = oracle_angle(x[b]);
 }
 
 /* The noise row a^(i)_t of width N (N a multiple of 4). */

@@ -6,7 +6,7 @@ Dust").  The oracle realises it as Philox4x32-10 (Salmon et al., SC'11) +
 Box-Muller (1958).  Pinned here against things other than the oracle itself:
   - the raw Philox stream against two independent open-source implementations
     compiled on this host (ATen's PhiloxRNGEngine, rocRAND's philox4x32_10),
-  - the uniform map by exact integer arithmetic,
+  - the uniform (radius) and angle maps by exact integer arithmetic,
   - Box-Muller by inverting it (radius and angle give back the uniforms) and by
     the distribution (moments, Kolmogorov-Smirnov against scipy's normal),
     with neighbouring coordinates uncorrelated.
@@ -86,23 +86,45 @@ def test_uniform_map_exact():
     assert np.array_equal(u.astype(np.float32).astype(np.float64), u)  # exact in fp32
 
 
+def test_angle_map_exact():
+    # v = m / 2^23 with m the top 23 bits: [0, 1) revolutions, 0 included
+    x = np.array([0, 1, 511, 512, 0x7FFFFFFF, 0x80000000, 0xFFFFFE00, 0xFFFFFFFF], dtype=np.uint32)
+    x = np.concatenate([x, np.random.default_rng(2).integers(0, 2**32, 100_000, dtype=np.uint64).astype(np.uint32)])
+    v = oracle.angle(x)
+    m = v * 2.0**23
+    assert np.array_equal(m, np.floor(m))
+    assert np.array_equal(m.astype(np.int64), (x >> 9).astype(np.int64))
+    assert (v >= 0).all() and (v < 1).all()
+    assert v[x == 511][0] == 0 and v[x == 512][0] == 2.0**-23
+    assert v[x == 0xFFFFFFFF][0] == 1 - 2.0**-23
+    assert np.array_equal(v.astype(np.float32).astype(np.float64), v)  # exact in fp32
+    # the radius uniform of the same word is the angle plus half a step
+    assert np.array_equal(oracle.uniform(x), v + 2.0**-24)
+
+
 def test_box_muller_inverts_to_the_block_uniforms():
-    # a[4j]^2 + a[4j+1]^2 = -2 ln u0 and atan2(a[4j+1], a[4j]) = 2 pi u1 (mod 2 pi);
-    # likewise columns 4j+2, 4j+3 with u2, u3.  This fixes which Philox word
-    # feeds which column.
+    # a[4j]^2 + a[4j+1]^2 = -2 ln u0 and atan2(a[4j+1], a[4j]) = 2 pi v1 (mod 2 pi),
+    # u0 the uniform of word 0 and v1 the angle of word 1; likewise columns
+    # 4j+2, 4j+3 with words 2 and 3.  This fixes which Philox word feeds which
+    # column and which map each word goes through.
     seed, stream, T, N, ndraw = 5, 3, 7, 64, 3
     a = oracle.noise(seed, stream, 0, ndraw, T, N)
     for i in range(ndraw):
         for t in range(T):
             ctr = np.array([[t, j, i, stream] for j in range(N // 4)], dtype=np.uint32)
-            u = oracle.uniform(oracle.philox4x32_10(seed, ctr).ravel()).reshape(-1, 4)
+            words = oracle.philox4x32_10(seed, ctr).ravel()
+            u = oracle.uniform(words).reshape(-1, 4)
+            v = oracle.angle(words).reshape(-1, 4)
             row = a[i, t].reshape(-1, 4)
             for p in (0, 1):
                 c, s = row[:, 2 * p], row[:, 2 * p + 1]
                 np.testing.assert_allclose(c * c + s * s, -2 * np.log(u[:, 2 * p]), rtol=1e-12)
                 ang = np.mod(np.arctan2(s, c) / (2 * np.pi), 1.0)
-                d = np.abs(ang - u[:, 2 * p + 1])
+                d = np.abs(ang - v[:, 2 * p + 1])
                 assert np.minimum(d, 1 - d).max() < 1e-12
+                # half a step of 2^-23 off: the uniform map in the angle is caught
+                d_u = np.abs(ang - u[:, 2 * p + 1])
+                assert np.minimum(d_u, 1 - d_u).min() > 2.0**-25
 
 
 def test_noise_draw_offset():

@@ -33,6 +33,7 @@ COS_MIN = 0.99999
 def assert_parity(gpu, ref, what: str, rel=REL_L2_MAX, cos=COS_MIN):
     r = rel_l2(gpu, ref)
     c = cosine(gpu, ref)
+    print(f"[parity] {what}: rel_l2={r:.3e} cos={c:.8f}", flush=True)
     assert r <= rel and c >= cos, f"{what}: rel_l2={r:.3e} cos={c:.8f}"
 
 
