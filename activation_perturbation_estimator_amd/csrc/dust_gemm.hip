@@ -442,12 +442,19 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
                                                      const float* __restrict__ g32,
                                                      const void* __restrict__ X, int x_bf16,
                                                      float* __restrict__ G) {
-  __shared__ int any;
-  if (threadIdx.x == 0) any = 0;
-  __syncthreads();
-  for (int64_t q = threadIdx.x; q < nsplit; q += 256)
-    if (count[q] != 0) any = 1;
-  __syncthreads();
+  // Whether any split left tokens to the exact pass: the counts are the same
+  // for every thread, read without a barrier so that their latency overlaps the
+  // partial loads below; the first 8 in one go (the count region holds at
+  // least 64 entries, so reading 8 stays inside it).
+  int any = 0;
+  {
+    const int4 c0 = reinterpret_cast<const int4*>(count)[0];
+    const int4 c1 = reinterpret_cast<const int4*>(count)[1];
+    const int c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) any |= (q < nsplit) ? c[q] : 0;
+    for (int64_t q = 8; q < nsplit; ++q) any |= count[q];
+  }
   const int64_t n = M * d;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * e4 < n; e4 += stride) {
