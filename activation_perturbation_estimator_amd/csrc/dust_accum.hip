@@ -9,8 +9,8 @@
 //
 // One workgroup per token (W waves split the columns as in the head kernels);
 // the draws run in a loop with the token's row of g in registers.  The rewards
-// of 64 draws are fetched at once (lane l holds draw i0+l) and broadcast one at
-// a time with v_readlane.
+// of 64 draws are fetched at once (lane l holds draw i0+l), one block of 64
+// ahead of their use, and broadcast one at a time with v_readlane.
 #include "dust_device.hpp"
 #include "dust_gemm16.hpp"
 #include "dust_launch.hpp"
@@ -33,10 +33,14 @@ error_estimate_kernel(const float* __restrict__ r, int64_t K, int64_t T, int64_t
 #pragma unroll
   for (int q = 0; q < kCols; ++q) acc[q] = 0.f;
 
+  float r_next = (lane < K) ? r[(int64_t)lane * T + t] : 0.f;
   float r_vec = 0.f;
   for (int64_t i = 0; i < K; ++i) {
     const int il = (int)(i & 63);
-    if (il == 0) r_vec = (i + lane < K) ? r[(i + lane) * T + t] : 0.f;
+    if (il == 0) {
+      r_vec = r_next;
+      r_next = (i + 64 + lane < K) ? r[(i + 64 + lane) * T + t] : 0.f;
+    }
     const float ri = lane_value(r_vec, il);
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
