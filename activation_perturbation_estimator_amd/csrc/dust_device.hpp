@@ -176,8 +176,9 @@ __device__ __forceinline__ float dpp_f(float v) {
 
 // Row sums R0..R3 in every lane of their row, then row_bcast:15 adds R0 into
 // row 1 and R2 into row 3, and row_bcast:31 adds row 1's R0 + R1 into row 3:
-// lane 63 holds (R2 + R3) + (R0 + R1).
-__device__ __forceinline__ float wave_sum(float v) {
+// lane 63 holds (R2 + R3) + (R0 + R1).  The sum is left in lane 63 only, for a
+// caller that stores it from that lane.
+__device__ __forceinline__ float wave_sum_lane63(float v) {
   v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
@@ -190,7 +191,12 @@ __device__ __forceinline__ float wave_sum(float v) {
                : "+v"(v));
   asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
                : "+v"(v));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return v;
+}
+
+// The wave's sum in every lane (read from lane 63 into a scalar register).
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum_lane63(v)), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -92,13 +92,14 @@ __device__ __forceinline__ float group_max(float wave_val, float* red, int slot)
   }
 }
 
-// Workgroup sums of kN wave-uniform values at once (one barrier).  Slot `slot`
-// of a kStride-wide layout; alternating slots need no second barrier.
+// Workgroup sums of kN per-wave values at once (one barrier); each wave's value
+// must be complete in its lane 63 (wave_sum_lane63), which stores it.  Slot
+// `slot` of a kStride-wide layout; alternating slots need no second barrier.
 template <int W, int kN, int kStride>
 __device__ __forceinline__ void group_sum_n(float* v, float* red, int slot) {
   if constexpr (W > 1) {
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
+    if ((threadIdx.x & 63) == 63) {  // the wave's sum is complete in lane 63
 #pragma unroll
       for (int d = 0; d < kN; ++d) red[(slot * kStride + d) * W + w] = v[d];
     }
@@ -263,7 +264,10 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
     float a[kDraws][kCols];
     float S[kDraws];
 #pragma unroll
-    for (int d = 0; d < kDraws; ++d) S[d] = wave_sum(draw_noise(i + d, a[d]));
+    for (int d = 0; d < kDraws; ++d) {
+      if constexpr (kW > 1) S[d] = wave_sum_lane63(draw_noise(i + d, a[d]));
+      else S[d] = wave_sum(draw_noise(i + d, a[d]));
+    }
     group_sum_n<kW, kDraws, kDraws>(S, red_loop, parity);
 #pragma unroll
     for (int d = 0; d < kDraws; ++d) finish(i + d, S[d], a[d]);
