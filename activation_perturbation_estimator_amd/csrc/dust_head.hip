@@ -180,7 +180,8 @@ head_kernel(const ZT* __restrict__ logits, const int32_t* __restrict__ targets, 
   }
   const float zty = fmaf(zy, kLog2e, -Ml2e);  // ztilde of the target column
   const float ell0 = kLn2 * (__builtin_amdgcn_logf(S0) - zty);
-  if constexpr (kZInLds) __syncthreads();
+  // No barrier for the staged row: each lane reads back only the columns it
+  // wrote itself, and a wave's LDS accesses complete in order.
 
   // The noise arrives divided by kBoxMullerScale (normal4_scaled): every use
   // scales it, so the constant rides on the scalar factors below and on g_t.
