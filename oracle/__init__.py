@@ -185,8 +185,10 @@ def head_estimate(logits, targets, X, seq_len: int, sigma: float, K: int, gamma:
     section), then the credit assignment of the paper digest, section 2.2.
 
     Returns (g_hat [T,V], G_W [V,d]) and, with diagnostics, a dict with
-    ell [K,T], c [K,T], r [K,T], ell0 [T] and g_scale [T,V], the magnitude
-    (1/(K sigma)) sum_i |r_i a_i| of the terms each element of g_hat sums."""
+    ell [K,T], c [K,T], r [K,T], ell0 [T] and g_scale [T,V], the scale of the
+    rounding error of each element of g_hat: (1/(K sigma)) sum_i (|r_i| +
+    max_j |r_j|) |a_i|, the magnitude of its terms plus the same with every
+    reward replaced by the token's largest."""
     z = _f64c(logits)
     y = np.ascontiguousarray(np.asarray(targets, dtype=np.int32))
     Xd = _f64c(X)
@@ -214,7 +216,7 @@ def head_rows(logits, targets, seq_len: int, sigma: float, K: int, gamma: float,
               with_scale: bool = False):
     """Error-estimate rows g_hat[tokens, :] of the LM-head estimator, computed
     token by token (same steps as head_estimate).  With with_losses the
-    per-draw losses [K, n] follow; with with_scale the term magnitudes
+    per-draw losses [K, n] follow; with with_scale the error scales
     (1/(K sigma)) sum_i |r_i a_i| of the same rows [n, V] come last."""
     z = _f64c(logits)
     y = np.ascontiguousarray(np.asarray(targets, dtype=np.int32))
@@ -236,7 +238,7 @@ def linear_estimate(X, c, seq_len: int, N: int, sigma: float, gamma: float, seed
                     stream: int = 0, with_r: bool = False, with_scale: bool = False):
     """Hidden linear layer: caller's centred loss decreases c [K,T] -> reward scan,
     error estimate and outer product (paper digest, section 2.2).  Returns
-    (g_hat, G_W), then r [K,T] with with_r, then the term magnitudes of g_hat
+    (g_hat, G_W), then r [K,T] with with_r, then the error scales of g_hat
     [T,N] with with_scale."""
     Xd = _f64c(X)
     cd = _f64c(c)
@@ -257,7 +259,7 @@ def linear_estimate(X, c, seq_len: int, N: int, sigma: float, gamma: float, seed
 def linear_rows(c, seq_len: int, N: int, sigma: float, gamma: float, seed: int, tokens,
                 stream: int = 0, with_scale: bool = False):
     """Error-estimate rows g_hat[tokens, :] of the linear-layer estimator (and,
-    with with_scale, the term magnitudes of the same rows)."""
+    with with_scale, the error scales of the same rows)."""
     cd = _f64c(c)
     K, T = cd.shape
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))

@@ -208,9 +208,13 @@ void oracle_reward_scan(const double* c, int64_t K, int64_t T, int64_t L, double
 /* Error estimate of token t ([P2] section 2.2):
  * g_t = -(1/(K sigma)) sum_i r^(i)_t a^(i)_t, a regenerated from its counters.
  * r^(i)_t is read at r[i * r_stride + r_col]; t keys the noise.
- * s_row (NULL to skip) receives the magnitude of the same sum's terms,
- * (1/(K sigma)) sum_i |r^(i)_t a^(i)_t|, the scale that a rounding error in
- * any one term is measured against; it does not enter g. */
+ * s_row (NULL to skip) receives the scale that a rounding error of the sum is
+ * measured against; it does not enter g.  It is the magnitude of the sum's
+ * terms plus the same with every reward replaced by the token's largest,
+ * (1/(K sigma)) sum_i (|r^(i)_t| + max_j |r^(j)_t|) |a^(i)_t|: a reward computed
+ * in single precision (a loss change formed from a ratio of exp sums, or a
+ * discounted scan) errs by a fraction of the token's largest reward, whatever
+ * the size of the reward itself. */
 static void error_estimate_token(const double* r, int64_t K, int64_t r_stride, int64_t r_col,
                                  int64_t t, int64_t N, double sigma, uint64_t seed,
                                  uint32_t stream, double* g_row, double* a_scratch,
@@ -218,11 +222,15 @@ static void error_estimate_token(const double* r, int64_t K, int64_t r_stride, i
 {
     for (int64_t n = 0; n < N; ++n) g_row[n] = 0.0;
     if (s_row) for (int64_t n = 0; n < N; ++n) s_row[n] = 0.0;
+    double rmax = 0.0;
+    if (s_row)
+        for (int64_t i = 0; i < K; ++i) rmax = fmax(rmax, fabs(r[i * r_stride + r_col]));
     for (int64_t i = 0; i < K; ++i) {
         double rit = r[i * r_stride + r_col];
         noise_row(seed, stream, i, t, N, a_scratch);
         for (int64_t n = 0; n < N; ++n) g_row[n] += rit * a_scratch[n];
-        if (s_row) for (int64_t n = 0; n < N; ++n) s_row[n] += fabs(rit * a_scratch[n]);
+        if (s_row)
+            for (int64_t n = 0; n < N; ++n) s_row[n] += (fabs(rit) + rmax) * fabs(a_scratch[n]);
     }
     double scale = -1.0 / ((double)K * sigma);
     for (int64_t n = 0; n < N; ++n) g_row[n] *= scale;

@@ -1,6 +1,7 @@
 """dust_head_estimate (LM head on cached logits) against the oracle: g_hat and
 G_W within relative L2 1e-3 / cosine 0.99999 as whole arrays and g_hat row by
-row, every element of g_hat within 1e-4 of the magnitude of the terms it sums
+row, every element of g_hat within 1e-4 of its error scale (the magnitude of
+the terms it sums, plus the same at the token's largest reward)
 and every element of G_W within 8 x 2^-11 of its root-sum-square scale, and
 per-draw losses within 2e-4 nats.
 

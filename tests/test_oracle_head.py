@@ -122,13 +122,15 @@ def test_rows_agree_with_full_estimate(gamma):
     tok = [0, 3, 5, 6, 11]
     rows = oracle.head_rows(z, y, L, 0.3, K, gamma, 2, tok)
     np.testing.assert_allclose(rows, g[tok], rtol=1e-12, atol=1e-14)
-    # the term magnitudes (1/(K sigma)) sum_i |r_i a_i|: the rows form agrees
-    # with the full estimate's, and numpy rebuilds them from r and the noise
+    # the error scales (1/(K sigma)) sum_i (|r_i| + max_j |r_j|) |a_i|: the rows
+    # form agrees with the full estimate's, and numpy rebuilds them from r and
+    # the noise
     _, _, diag = oracle.head_estimate(z, y, X, L, 0.3, K, gamma, 2, diagnostics=True)
     rows2, srows = oracle.head_rows(z, y, L, 0.3, K, gamma, 2, tok, with_scale=True)
     np.testing.assert_allclose(srows, diag["g_scale"][tok], rtol=1e-12, atol=1e-14)
     a = oracle.noise(2, 0, 0, K, T, V)
-    ref = np.abs(diag["r"][:, :, None] * a).sum(0) / (K * 0.3)
+    r = np.abs(diag["r"])
+    ref = ((r + r.max(0, keepdims=True))[:, :, None] * np.abs(a)).sum(0) / (K * 0.3)
     np.testing.assert_allclose(diag["g_scale"], ref, rtol=1e-12, atol=1e-14)
     assert (np.abs(g) <= diag["g_scale"] * (1 + 1e-12)).all()
 

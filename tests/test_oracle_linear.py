@@ -120,10 +120,12 @@ def test_perturbed_linear_is_product_plus_noise():
 
 
 def test_term_magnitudes():
-    # The oracle's per-element scale (1/(K sigma)) sum_i |r_i a_i| (the bound
-    # that GPU rounding errors are measured against): numpy from the pinned
-    # noise stream and the pinned scan, the triangle inequality |g| <= scale,
-    # equality for a one-hot c, and the same values from the rows form.
+    # The oracle's per-element error scale (1/(K sigma)) sum_i (|r_i| + max_j
+    # |r_j|) |a_i| (the bound that GPU rounding errors are measured against):
+    # numpy from the pinned noise stream and the pinned scan, the triangle
+    # inequality |g| <= scale, the closed form for a one-hot c (|g| plus the
+    # one reward's size times the noise magnitudes), and the same values from
+    # the rows form.
     K, T, L, N, d, sigma, gamma, seed = 6, 12, 4, 8, 3, 0.3, 0.7, 9
     rng = np.random.default_rng(6)
     X = rng.standard_normal((T, d))
@@ -131,12 +133,16 @@ def test_term_magnitudes():
     g, _, r, s = oracle.linear_estimate(X, c, L, N, sigma, gamma, seed, with_r=True,
                                         with_scale=True)
     a = oracle.noise(seed, 0, 0, K, T, N)
-    ref = np.abs(r[:, :, None] * a).sum(0) / (K * sigma)
+    ra = np.abs(r)
+    ref = ((ra + ra.max(0, keepdims=True))[:, :, None] * np.abs(a)).sum(0) / (K * sigma)
     np.testing.assert_allclose(s, ref, rtol=1e-12, atol=0)
     assert (np.abs(g) <= s * (1 + 1e-12)).all()
     rows, srows = oracle.linear_rows(c, L, N, sigma, gamma, seed, [1, 7], with_scale=True)
     np.testing.assert_allclose(srows, s[[1, 7]], rtol=1e-12)
     c1 = np.zeros((K, T))
     c1[2, 5] = 1.5
-    g1, _, s1 = oracle.linear_estimate(X, c1, L, N, sigma, gamma, seed, with_scale=True)
-    np.testing.assert_allclose(s1, np.abs(g1), rtol=1e-12, atol=0)
+    g1, _, r1, s1 = oracle.linear_estimate(X, c1, L, N, sigma, gamma, seed, with_r=True,
+                                           with_scale=True)
+    rmax = np.abs(r1).max(0)[:, None]
+    np.testing.assert_allclose(s1, np.abs(g1) + rmax * np.abs(a).sum(0) / (K * sigma),
+                               rtol=1e-12, atol=0)

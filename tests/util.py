@@ -78,10 +78,12 @@ def assert_elementwise(gpu, ref, scale, what: str, c: float, atol: float = 0.0):
 
 
 # g_hat: each element sums K terms r_i a_i / (K sigma); fp32 evaluation errs by
-# ~1e-6 of the terms' magnitude sum_i |r_i a_i| / (K sigma), so 1e-4 of it is
-# far above rounding and far below one dropped or wrong term (1/K of it, K <=
-# 2^14 in the tests at full size; larger K only at sampled rows with the same
-# bound scaled, see callers).
+# ~1e-6 of the terms' magnitude sum_i |r_i a_i| / (K sigma), plus, since the
+# rewards themselves are single precision (a loss change from a ratio of exp
+# sums, a discounted scan), a floor of ~1e-7 of the token's largest reward on
+# every term: the oracle's scale is (1/(K sigma)) sum_i (|r_i| + max_j |r_j|)
+# |a_i|.  1e-4 of it is far above rounding and far below a wrong column, lane
+# share or row.
 G_HAT_TERM_TOL = 1e-4
 # G_W from the composed calls: each element sums T products g_t x_t whose
 # operands the matrix cores take rounded to 11 significant bits (relative error
