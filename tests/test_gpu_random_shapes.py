@@ -1,10 +1,14 @@
-"""Seeded random shapes against the oracle: LM-head and hidden-layer estimates
-whose sequence length, token count, width, vocabulary, population, discount,
-sigma, dtypes, seed and stream are drawn from one generator per case (seeded
-by the case number), each held to the same bar as the fixed-shape tests: whole
-arrays and every row of g_hat within relative L2 1e-3 and cosine 0.99999,
-every element of g_hat within its term scale, and G_W against the fp64 product
-(paper digest, section 2.2, for both estimates)."""
+"""Seeded random shapes against the oracle, one generator per case (seeded by
+the case number):
+  - the LM-head and hidden-layer estimates (paper digest, section 2.2): sequence
+    length, token count, width, vocabulary, population, discount, sigma, dtypes,
+    seed and stream drawn at random; whole arrays and every row of g_hat within
+    relative L2 1e-3 and cosine 0.99999, every element of g_hat within 1e-4 of
+    its error scale, and G_W against the fp64 product;
+  - the outer product over token rows spanning many binades (some left to the
+    exact fp32 pass);
+  - the reward scan, element by element against the size of what it sums;
+  - the embedding estimate, row by row against the size of what it sums."""
 import numpy as np
 import pytest
 
@@ -71,3 +75,67 @@ def test_linear_random_shape(case):
     assert_elementwise(g, rg, sc, "g_hat elements", G_HAT_TERM_TOL)
     assert_parity(G, rG, "G_W")
     assert_gw(G, rg, synth.to_f64(X))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_outer_sum_random_shape(case):
+    """dust_outer_sum on random shapes whose token rows span many binades (the
+    per-token power-of-two scaling of the fp16 pass), with some tokens whose
+    range no scale fits (left to the exact fp32 pass)."""
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(3000 + case)
+    T, N, d = int(rng.integers(1, 6000)), int(rng.integers(1, 1500)), int(rng.integers(1, 700))
+    bf16 = bool(rng.integers(0, 2))
+    print(f"[random outer sum] case {case}: T={T} N={N} d={d} bf16={bf16}", flush=True)
+    g = rng.standard_normal((T, N)) * np.exp2(rng.uniform(-30, 30, (T, 1)))
+    g[rng.random(T) < 0.02] *= 2.0**-60  # products below what fp16 holds after scaling
+    g = g.astype(np.float32)
+    Xf = (rng.standard_normal((T, d)) * np.exp2(rng.uniform(-10, 10, (T, 1)))).astype(np.float32)
+    X = torch.from_numpy(Xf).to(torch.bfloat16) if bf16 else torch.from_numpy(Xf)
+    G = dust.outer_sum(torch.from_numpy(g).cuda(), X.cuda())
+    torch.cuda.synchronize()
+    assert_gw(G.cpu().numpy(), g.astype(np.float64), synth.to_f64(X))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_reward_scan_random_shape(case):
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(4000 + case)
+    L = int(rng.choice([1, 2, 5, 63, 64, 255, 256, 1000, 2048, 4097, 9000]))
+    T = L * int(rng.integers(1, 4))
+    K = int(rng.integers(1, 9))
+    gamma = float(rng.choice([0.0, 0.3, 0.9, 1.0]))
+    print(f"[random scan] case {case}: K={K} T={T} L={L} gamma={gamma}", flush=True)
+    c = rng.standard_normal((K, T)).astype(np.float32)
+    r = dust.reward_scan(torch.from_numpy(c).cuda(), seq_len=L, gamma=gamma)
+    torch.cuda.synchronize()
+    got = r.cpu().numpy()
+    if gamma == 0.0:
+        assert np.array_equal(got, c)
+    else:
+        ref = oracle.reward_scan(c.astype(np.float64), L, gamma)
+        # per sequence: the recurrence's fp32 rounding against the size of what it sums
+        scale = oracle.reward_scan(np.abs(c).astype(np.float64), L, gamma)
+        assert (np.abs(got - ref) <= 1e-5 * scale + 1e-30).all()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_embedding_random_shape(case):
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(5000 + case)
+    T, N, vocab = int(rng.integers(1, 40000)), 4 * int(rng.integers(1, 130)), int(rng.integers(1, 9000))
+    print(f"[random embedding] case {case}: T={T} N={N} vocab={vocab}", flush=True)
+    ids = synth.zipf_targets(rng, T, vocab) if rng.integers(0, 2) else \
+        rng.integers(-2, vocab + 2, T).astype(np.int32)
+    g = rng.standard_normal((T, N)).astype(np.float32)
+    G = dust.embedding_grad(torch.from_numpy(ids).cuda(), torch.from_numpy(g).cuda(), vocab)
+    torch.cuda.synchronize()
+    G = G.cpu().numpy()
+    ref = oracle.embedding_grad(ids, g.astype(np.float64), vocab)
+    # each row sums its tokens' rows in fp32: within 1e-5 of the sum of magnitudes
+    absref = oracle.embedding_grad(ids, np.abs(g).astype(np.float64), vocab)
+    assert (np.abs(G - ref) <= 1e-5 * absref).all()
+    assert (G[absref == 0] == 0).all()
