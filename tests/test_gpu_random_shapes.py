@@ -8,7 +8,8 @@ the case number):
   - the outer product over token rows spanning many binades (some left to the
     exact fp32 pass);
   - the reward scan, element by element against the size of what it sums;
-  - the embedding estimate, row by row against the size of what it sums."""
+  - the embedding estimate, row by row against the size of what it sums;
+  - the perturbed forward, element by element against the product's size."""
 import numpy as np
 import pytest
 
@@ -139,3 +140,30 @@ def test_embedding_random_shape(case):
     absref = oracle.embedding_grad(ids, np.abs(g).astype(np.float64), vocab)
     assert (np.abs(G - ref) <= 1e-5 * absref).all()
     assert (G[absref == 0] == 0).all()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_forward_random_shape(case):
+    """The perturbed forward Y[k] = X W^T + sigma a^(draw0+k) on random shapes,
+    draw offsets, streams and seeds, element by element: within 1e-4 of the
+    product's magnitude sum_j |x_j w_j| plus 1e-5 of sigma (the noise in fp32)."""
+    dust = need_gpu()
+    import torch
+    rng = np.random.default_rng(6000 + case)
+    # the call takes d % 8 == 0 and N % 4 == 0
+    T, d, N = int(rng.integers(1, 700)), 8 * int(rng.integers(1, 40)), 4 * int(rng.integers(1, 300))
+    ndraw, draw0 = int(rng.integers(1, 5)), int(rng.integers(0, 2**31))
+    stream, seed = int(rng.integers(0, 2**32)), int(rng.integers(0, 2**63))
+    bf16 = bool(rng.integers(0, 2))
+    sigma = float(rng.choice([0.01, 0.1, 1.0]))
+    print(f"[random forward] case {case}: T={T} d={d} N={N} ndraw={ndraw} bf16={bf16}", flush=True)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    X = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32) / np.sqrt(d)).to(dt)
+    W = torch.from_numpy(rng.standard_normal((N, d)).astype(np.float32) / np.sqrt(d)).to(dt)
+    Y = dust.perturbed_linear(X.cuda(), W.cuda(), sigma=sigma, seed=seed, stream=stream,
+                              draw0=draw0, ndraw=ndraw)
+    torch.cuda.synchronize()
+    Xd, Wd = synth.to_f64(X), synth.to_f64(W)
+    ref = oracle.perturbed_linear(Xd, Wd, sigma, seed, stream, draw0, ndraw)
+    mag = np.abs(Xd) @ np.abs(Wd).T
+    assert (np.abs(Y.cpu().numpy() - ref) <= 1e-4 * mag[None] + 1e-5 * sigma).all()
