@@ -374,13 +374,16 @@ def ce_grad(logits, targets, out=None):
     return o
 
 
-def check_targets(targets, V: int) -> bool:
-    """True when 0 <= targets < V everywhere (waits for the device)."""
+def check_targets(targets, V: int, flag=None) -> bool:
+    """True when 0 <= targets < V everywhere (waits for the device).  ``flag``:
+    a device int32 tensor the call may overwrite, or None for the library's own."""
     torch = _torch()
     _expect(targets, "targets", dtypes=torch.int32)
-    flag = torch.empty(1, dtype=torch.int32, device=targets.device)
+    if flag is not None:
+        _expect(flag, "flag", (1,), torch.int32, targets.device)
     st = _lib.load().dust_check_targets(_dev(targets, "targets"), targets.numel(), int(V),
-                                        flag.data_ptr(), _stream(targets.device))
+                                        None if flag is None else flag.data_ptr(),
+                                        _stream(targets.device))
     if st == _lib.DUST_ERR_TARGETS:
         return False
     _lib.check("dust_check_targets", st)

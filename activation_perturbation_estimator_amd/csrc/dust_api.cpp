@@ -408,7 +408,8 @@ dust_status dust_ce_grad(const void* logits, dust_dtype dt, const int32_t* targe
 
 dust_status dust_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
                                dust_stream_t s_) {
-  if (!targets || !flag || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;
+  if (!targets || T < 0 || V <= 0) return DUST_ERR_INVALID_ARG;
+  if (flag == nullptr && dust::check_targets_own_flag(&flag) != hipSuccess) return DUST_ERR_HIP;
   hipStream_t s = as_stream(s_);
   if (dust::launch_check_targets(targets, T, V, flag, s) != hipSuccess) return DUST_ERR_HIP;
   int32_t h = 0;

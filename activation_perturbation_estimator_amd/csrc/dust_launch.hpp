@@ -91,6 +91,8 @@ hipError_t launch_ce_grad(const void* logits, bool bf16, const int32_t* targets,
                           int64_t V, float* out, hipStream_t s);
 
 // Target range check; flag must be a device int32.
+// The library's own flag for dust_check_targets on the current device.
+hipError_t check_targets_own_flag(int32_t** out);
 hipError_t launch_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
                                 hipStream_t s);
 

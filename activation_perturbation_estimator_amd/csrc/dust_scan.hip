@@ -8,6 +8,8 @@
 // perturbation into another sequence, so the scan restarts at every sequence
 // boundary.  Centring is read as: subtract the mean over the K draws of the
 // same token.
+#include <mutex>
+
 #include "dust_device.hpp"
 #include "dust_launch.hpp"
 
@@ -403,6 +405,34 @@ hipError_t launch_reward_scan(const float* c, int64_t K, int64_t T, int64_t L, f
     hipLaunchKernelGGL((reward_scan_kernel<false, int64_t>), grid, dim3(kScanThreads), 0, s, c,
                        nseg, L, gamma, r);
   return hipGetLastError();
+}
+
+// The flag of dust_check_targets calls that pass none: one int32 per GPU, held
+// until the process ends.  Host code takes each device's address of it once,
+// with hipGetSymbolAddress, and passes that to the kernels.
+static __device__ int32_t check_flag;
+
+namespace {
+constexpr int kMaxFlagDevices = 64;
+std::mutex g_flag_mutex;
+int32_t* g_flag_ptr[kMaxFlagDevices] = {};
+}  // namespace
+
+hipError_t check_targets_own_flag(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxFlagDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_flag_mutex);
+  if (g_flag_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_flag));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_flag_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_flag_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,

@@ -19,8 +19,9 @@
  *   - Pointers named as device pointers are HIP device memory owned by the
  *     caller.  The library allocates nothing and keeps no state between calls,
  *     so calls on different streams may run concurrently (they must not share
- *     output or workspace buffers).  The one exception is
- *     dust_embedding_grad_noalloc, whose scratch is a fixed array per GPU.
+ *     output or workspace buffers).  The exceptions are
+ *     dust_embedding_grad_noalloc, whose scratch is a fixed array per GPU, and
+ *     dust_check_targets with a NULL flag, which uses one int32 per GPU.
  *   - Calls enqueue kernels on the caller's stream `s` and return without
  *     waiting, except dust_check_targets, which waits for its own result.
  *     Outputs are overwritten, never accumulated.
@@ -308,7 +309,8 @@ dust_status dust_ce_grad(const void* logits, dust_dtype dt, const int32_t* targe
 
 /* Checks 0 <= targets[t] < V for all t; waits on s for the answer.
  * Returns DUST_OK or DUST_ERR_TARGETS.  `flag` is a device int32 the call
- * overwrites (caller-owned scratch). */
+ * overwrites (caller-owned scratch), or NULL for the library's own flag, one
+ * per GPU: calls with NULL that overlap on one GPU race. */
 dust_status dust_check_targets(const int32_t* targets, int64_t T, int64_t V, int32_t* flag,
                                dust_stream_t s);
 

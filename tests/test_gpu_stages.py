@@ -165,15 +165,20 @@ def test_outer_sum(T, N, d, bf16):
     _check_outer(G.cpu().numpy(), ref, g, synth.to_f64(X))
 
 
-def test_check_targets():
+@pytest.mark.parametrize("own_flag", [True, False])
+def test_check_targets(own_flag):
+    """With the library's own flag (NULL) or a caller's, which starts dirty."""
     dust = need_gpu()
     import torch
+    flag = None if own_flag else torch.full((1,), 7, dtype=torch.int32, device="cuda")
     y = torch.randint(0, 100, (1000,), dtype=torch.int32, device="cuda")
-    assert dust.check_targets(y, 100)
+    assert dust.check_targets(y, 100, flag)
     y[517] = 100
-    assert not dust.check_targets(y, 100)
+    assert not dust.check_targets(y, 100, flag)
     y[517] = -1
-    assert not dust.check_targets(y, 100)
+    assert not dust.check_targets(y, 100, flag)
+    y[517] = 5
+    assert dust.check_targets(y, 100, flag)  # the flag is cleared by every call
 
 
 @pytest.mark.parametrize("L,gamma", [(1024, 0.9), (1000, 0.9), (256, 1.0), (260, 0.5),
